@@ -1,0 +1,378 @@
+"""Pins for the fp64 oracle: checked against things other than itself.
+
+Nothing here touches the GPU or the HIP library.  Each test names what fixes
+the expected value: a 60-digit mpmath brute force, a library routine
+(torch's float64 CPU scaled_dot_product_attention, logsumexp, softmax, its
+float8_e4m3fn cast), a closed form, or an invariant of softmax attention.
+"""
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+from workloads import make_block_mask, make_qkv
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _sdpa64(q, k, v, scale, bool_mask=None):
+    q, k, v = (t.to(torch.float64) for t in (q, k, v))
+    return F.scaled_dot_product_attention(q, k, v, attn_mask=bool_mask, scale=scale)
+
+
+def _expand_mask(mask, N, block=128):
+    """Block mask [nb, nb] -> boolean token mask [N, N] (True = attend)."""
+    idx = torch.arange(N) // block
+    return mask.bool()[idx][:, idx]
+
+
+# ----------------------------------------------------------------------------
+# dense attention
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,D", [(1, 8), (2, 8), (3, 5), (17, 8), (5, 128)])
+def test_attn_vs_mpmath_bruteforce(N, D):
+    """60-digit brute force: p_j = e^{s_j} / sum e^{s} with no max shift."""
+    g = torch.Generator().manual_seed(100 + N * 7 + D)
+    q, k, v = (torch.randn((1, 1, N, D), generator=g, dtype=torch.float64) for _ in range(3))
+    scale = 1.0 / math.sqrt(D)
+    o, lse = oracle.attn(q, k, v, scale)
+    mpmath.mp.dps = 60
+    Q, K, V = (t[0, 0].tolist() for t in (q, k, v))
+    for i in range(N):
+        s = [mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(Q[i][d]) * mpmath.mpf(K[j][d]) for d in range(D))
+             for j in range(N)]
+        e = [mpmath.exp(x) for x in s]
+        z = mpmath.fsum(e)
+        for d in range(D):
+            ref = mpmath.fsum(e[j] * mpmath.mpf(V[j][d]) for j in range(N)) / z
+            assert abs(o[0, 0, i, d] - float(ref)) <= 1e-13
+        assert abs(lse[0, 0, i] - float(mpmath.log(z))) <= 1e-13
+
+
+def test_attn_vs_torch_sdpa_tiny_workload():
+    """Library routine: torch float64 CPU SDPA on the tiny joint workload
+    (64 text + 256 image tokens, 2 heads), and torch.logsumexp for lse."""
+    q, k, v = make_qkv(1, 2, 320, 128, seed=0)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = oracle.attn(q, k, v, scale)
+    ref = _sdpa64(q, k, v, scale).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-12
+    logits = scale * (q.double() @ k.double().transpose(-1, -2))
+    ref_lse = torch.logsumexp(logits, dim=-1).numpy()
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-12
+
+
+def test_attn_large_logits_stay_finite():
+    """Logits of order 1e3 overflow a naive exp; the max shift must keep the
+    result finite and equal to SDPA."""
+    q, k, v = make_qkv(1, 1, 64, 128, seed=5)
+    q = q.double() * 60.0
+    scale = 1.0 / math.sqrt(128)
+    o, lse = oracle.attn(q, k, v, scale)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    ref = _sdpa64(q, k, v, scale).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-12
+
+
+def test_attn_peaked_keys_vs_sdpa():
+    """The x8 key rows of the 2048^2 workload, at a small N."""
+    q, k, v = make_qkv(1, 2, 400, 128, seed=0, peaked_key_frac=0.01)
+    scale = 1.0 / math.sqrt(128)
+    o, _ = oracle.attn(q, k, v, scale)
+    ref = _sdpa64(q, k, v, scale).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("N", [320, 257])
+def test_block_mask_vs_sdpa(N):
+    """Masked blocks are -inf logits: SDPA with the expanded boolean mask.
+    The mask is asymmetric, so a transposed (key, query) lookup fails."""
+    q, k, v = make_qkv(1, 2, N, 128, seed=3)
+    nb = (N + 127) // 128
+    mask = torch.zeros((nb, nb), dtype=torch.uint8)
+    mask.fill_diagonal_(1)
+    mask[0, nb - 1] = 1          # query block 0 also sees the ragged last block
+    mask[nb - 1, 1] = 1 if nb > 2 else 0
+    scale = 1.0 / math.sqrt(128)
+    o, lse = oracle.attn(q, k, v, scale, mask=mask)
+    bm = _expand_mask(mask, N)
+    ref = _sdpa64(q, k, v, scale, bm).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-12
+    logits = scale * (q.double() @ k.double().transpose(-1, -2))
+    ref_lse = torch.logsumexp(logits.masked_fill(~bm, -math.inf), dim=-1).numpy()
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-12
+
+
+def test_block_mask_per_head_stride():
+    """A different mask per (b, h) through mask_stride_bh."""
+    N = 300
+    q, k, v = make_qkv(1, 2, N, 128, seed=4)
+    nb = 3
+    m0 = make_block_mask(N, 0, 0.4, seed=1)
+    m1 = make_block_mask(N, 0, 0.4, seed=2)
+    masks = torch.stack([m0, m1])
+    scale = 1.0 / math.sqrt(128)
+    o, _ = oracle.attn(q, k, v, scale, mask=masks, mask_stride_bh=nb * nb)
+    for h, m in enumerate((m0, m1)):
+        ref = _sdpa64(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], scale, _expand_mask(m, N)).numpy()
+        assert np.max(np.abs(o[:, h:h + 1] - ref)) <= 1e-12
+
+
+def test_fully_masked_row_is_zero():
+    q, k, v = make_qkv(1, 1, 256, 128, seed=6)
+    mask = torch.tensor([[0, 0], [1, 1]], dtype=torch.uint8)
+    o, lse = oracle.attn(q, k, v, 0.1, mask=mask)
+    assert np.all(o[0, 0, :128] == 0.0)
+    assert np.all(np.isneginf(lse[0, 0, :128]))
+    assert np.all(np.isfinite(o[0, 0, 128:]))
+
+
+def test_rows_of_p_sum_to_one_and_equal_softmax():
+    """V = identity rows (N <= D) makes O the probability matrix itself."""
+    N, D = 17, 128
+    g = torch.Generator().manual_seed(11)
+    q, k = (torch.randn((1, 1, N, D), generator=g, dtype=torch.float64) for _ in range(2))
+    v = torch.zeros((1, 1, N, D), dtype=torch.float64)
+    v[0, 0, torch.arange(N), torch.arange(N)] = 1.0
+    scale = 1.0 / math.sqrt(D)
+    o, _ = oracle.attn(q, k, v, scale)
+    P = o[0, 0, :, :N]
+    assert np.max(np.abs(P.sum(axis=1) - 1.0)) <= 1e-12
+    ref = scipy.special.softmax(scale * (q[0, 0].numpy() @ k[0, 0].numpy().T), axis=1)
+    assert np.max(np.abs(P - ref)) <= 1e-14
+    assert np.all(o[0, 0, :, N:] == 0.0)
+
+
+def test_constant_v_returns_constant():
+    q, k, _ = make_qkv(1, 2, 300, 128, seed=7)
+    v = torch.full((1, 2, 300, 128), 0.375, dtype=torch.float64)
+    v[:, :, :, 5] = -2.5
+    o, _ = oracle.attn(q, k, v, 0.0883883)
+    assert np.max(np.abs(o[..., :5] - 0.375)) <= 1e-14
+    assert np.max(np.abs(o[..., 5] + 2.5)) <= 1e-14
+
+
+def test_key_value_permutation_invariance_and_query_equivariance():
+    q, k, v = make_qkv(1, 1, 200, 128, seed=8)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = oracle.attn(q, k, v, scale)
+    pk = torch.randperm(200, generator=torch.Generator().manual_seed(1))
+    o2, lse2 = oracle.attn(q, k[:, :, pk], v[:, :, pk], scale)
+    assert np.max(np.abs(o - o2)) <= 1e-13 and np.max(np.abs(lse - lse2)) <= 1e-13
+    pq = torch.randperm(200, generator=torch.Generator().manual_seed(2))
+    o3, _ = oracle.attn(q[:, :, pq], k, v, scale)
+    assert np.max(np.abs(o3 - o[:, :, pq.numpy()])) <= 1e-13
+
+
+def test_one_hot_dominant_key_selects_its_value_row():
+    N, D = 64, 128
+    q, k, v = make_qkv(1, 1, N, D, seed=9)
+    q, k, v = q.double(), k.double(), v.double()
+    i, j = 10, 37
+    k[0, 0, j] = 30.0 * q[0, 0, i]          # logit gap of order 30 |q_i|^2 / sqrt(D) >> 50
+    o, _ = oracle.attn(q, k, v, 1.0 / math.sqrt(D))
+    assert np.max(np.abs(o[0, 0, i] - v[0, 0, j].numpy())) <= 1e-15
+
+
+def test_single_token_and_zero_query():
+    q, k, v = make_qkv(1, 1, 1, 128, seed=10)
+    o, lse = oracle.attn(q, k, v, 0.1)
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0].double().numpy())
+    assert lse[0, 0, 0] == pytest.approx(0.1 * float((q.double() * k.double()).sum()), abs=1e-14)
+    q, k, v = make_qkv(1, 1, 150, 128, seed=11)
+    o, lse = oracle.attn(torch.zeros_like(q), k, v, 0.1)
+    assert np.max(np.abs(o[0, 0] - v[0, 0].double().numpy().mean(axis=0))) <= 1e-14
+    assert np.max(np.abs(lse - math.log(150))) <= 1e-14
+
+
+def test_sampled_rows_match_full():
+    q, k, v = make_qkv(1, 2, 330, 128, seed=12)
+    o, lse = oracle.attn(q, k, v, 0.0883883)
+    rows = np.array([0, 5, 329, 330, 659], dtype=np.int64)
+    os_, ls_ = oracle.attn(q, k, v, 0.0883883, rows=rows)
+    flat = o.reshape(-1, 128)
+    assert np.array_equal(os_, flat[rows]) and np.array_equal(ls_, lse.reshape(-1)[rows])
+
+
+# ----------------------------------------------------------------------------
+# OCP E4M3 codec
+# ----------------------------------------------------------------------------
+
+def _torch_decode_all():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_decode_exhaustive_vs_torch():
+    ref = _torch_decode_all()
+    mine = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e4m3_golden_points():
+    path = os.path.join(HERE, "golden", "e4m3_points.txt")
+    n = 0
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        code_s, val_s = line.split()
+        code, val = int(code_s, 16), float(val_s)
+        got = oracle.e4m3_decode(code)
+        if math.isnan(val):
+            assert math.isnan(got)
+        else:
+            assert got == val and math.copysign(1, got) == math.copysign(1, val)
+            assert oracle.e4m3_encode(val) == code
+        n += 1
+    assert n >= 10
+
+
+def test_e4m3_encode_all_bf16_vs_torch():
+    """Every finite bf16 bit pattern, clamped to +-448, encoded with RNE."""
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    x = bits.view(torch.bfloat16).to(torch.float32)
+    fin = torch.isfinite(x)
+    x = x[fin].clamp(-448.0, 448.0)
+    ref = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mine = np.array([oracle.e4m3_encode(float(t)) for t in x.tolist()], dtype=np.uint8)
+    assert np.array_equal(mine, ref)
+
+
+def test_e4m3_encode_ties_and_random_fp32_vs_torch():
+    ref_vals = _torch_decode_all()
+    fin = ref_vals[np.isfinite(ref_vals) & (ref_vals >= 0)]
+    fin = np.unique(fin)
+    mids = (fin[1:] + fin[:-1]) / 2.0        # exact ties between neighbours
+    g = np.random.default_rng(0)
+    rnd = np.concatenate([g.standard_normal(20000) * s for s in (1e-3, 0.05, 3.0, 150.0)])
+    x = np.concatenate([mids, -mids, rnd]).astype(np.float32)
+    x = np.clip(x, -448.0, 448.0)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mine = np.array([oracle.e4m3_encode(float(t)) for t in x], dtype=np.uint8)
+    assert np.array_equal(mine, ref)
+
+
+# ----------------------------------------------------------------------------
+# fp8 quantiser and recipe
+# ----------------------------------------------------------------------------
+
+def test_fp8_quantize_properties():
+    q, _, _ = make_qkv(1, 2, 300, 128, seed=13)
+    q[0, 1, 128:256] = 0            # an all-zero block
+    codes, scales = oracle.fp8_quantize(q)
+    x = q.to(torch.float32).numpy()
+    dec = oracle.e4m3_decode_array(codes)
+    for h in range(2):
+        for b, (j0, j1) in enumerate([(0, 128), (128, 256), (256, 300)]):
+            blk = x[0, h, j0:j1]
+            amax = np.float32(np.abs(blk).max())
+            c = codes[0, h, j0:j1]
+            if amax == 0:
+                assert scales[0, h, b] == 1.0 and np.all(c == 0)
+                continue
+            assert scales[0, h, b] == np.float32(amax / np.float32(448.0))
+            # the block maximum lands exactly on the largest code
+            assert np.max(np.abs(dec[0, h, j0:j1])) == 448.0
+            # dequantised values within half an e4m3 step (relative 2^-4) or
+            # half the subnormal step
+            y = blk.astype(np.float64) * float(np.float32(448.0) / amax)
+            err = np.abs(dec[0, h, j0:j1] - y)
+            assert np.all(err <= np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) + 1e-12)
+
+
+def test_fp8_quantize_vs_torch_cast():
+    q, _, _ = make_qkv(1, 3, 260, 128, seed=14)
+    codes, scales = oracle.fp8_quantize(q)
+    x = q.to(torch.float32)
+    for h in range(3):
+        for b, (j0, j1) in enumerate([(0, 128), (128, 256), (256, 260)]):
+            blk = x[0, h, j0:j1]
+            amax = blk.abs().max()
+            inv = torch.tensor(448.0, dtype=torch.float32) / amax
+            ref = (blk * inv).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(codes[0, h, j0:j1], ref)
+
+
+def _quantized_inputs(N, seed, H=1, peaked=0.0):
+    q, k, v = make_qkv(1, H, N, 128, seed=seed, peaked_key_frac=peaked)
+    q8, sq = oracle.fp8_quantize(q)
+    k8, sk = oracle.fp8_quantize(k)
+    v8, sv = oracle.fp8_quantize(v)
+    return (q, k, v), (q8, k8, v8, sq, sk, sv)
+
+
+def _dequant(codes, scales, block=128):
+    dec = oracle.e4m3_decode_array(codes)
+    s = np.repeat(scales.astype(np.float64), block, axis=-1)[..., :codes.shape[2]]
+    return dec * s[..., None]
+
+
+@pytest.mark.parametrize("N", [128, 300, 700])
+def test_fp8_recipe_without_p_quantisation_is_attention_on_dequantised_inputs(N):
+    """With P kept exact the running-max recipe must reduce to the textbook
+    definition on the dequantised Q, K, V (pins the block bookkeeping and
+    where each scale is applied)."""
+    _, (q8, k8, v8, sq, sk, sv) = _quantized_inputs(N, 15, H=2)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale, quantize_p=False)
+    qd, kd, vd = _dequant(q8, sq), _dequant(k8, sk), _dequant(v8, sv)
+    ref, ref_lse = oracle.attn(qd, kd, vd, scale)
+    sd = _sdpa64(*(torch.from_numpy(t) for t in (qd, kd, vd)), scale).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-12
+    assert np.max(np.abs(o - sd)) <= 1e-12
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-12
+
+
+def test_fp8_recipe_one_hot_key_returns_dequantised_value_row():
+    (q, k, v), _ = _quantized_inputs(200, 16)
+    i, j = 3, 150
+    k = k.clone()
+    k[0, 0, j] = (20.0 * q[0, 0, i].float()).to(torch.bfloat16)
+    q8, sq = oracle.fp8_quantize(q)
+    k8, sk = oracle.fp8_quantize(k)
+    v8, sv = oracle.fp8_quantize(v)
+    o, _ = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, 1.0 / math.sqrt(128))
+    vd = _dequant(v8, sv)
+    # P8 = e4m3(448) = 448 for the dominant key, every other weight rounds to 0
+    assert np.max(np.abs(o[0, 0, i] - vd[0, 0, j])) <= 1e-12
+
+
+def test_fp8_recipe_single_block_closed_form():
+    """N <= 128: one key block, so the running max is the row max and the
+    recipe is O = sum_j dec(e4m3(448 w_j)) / 448 * V_j / sum_j w_j."""
+    (q, k, v), (q8, k8, v8, sq, sk, sv) = _quantized_inputs(96, 17)
+    scale = 1.0 / math.sqrt(128)
+    o, _ = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale)
+    qd, kd, vd = _dequant(q8, sq)[0, 0], _dequant(k8, sk)[0, 0], _dequant(v8, sv)[0, 0]
+    t = scale * (qd @ kd.T)
+    w = np.exp(t - t.max(axis=1, keepdims=True))
+    p8 = torch.from_numpy((w.astype(np.float32) * np.float32(448.0))).to(torch.float8_e4m3fn)
+    p = p8.to(torch.float64).numpy() / 448.0
+    ref = (p @ vd) / w.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(o[0, 0] - ref)) <= 1e-12
+
+
+def test_fp8_recipe_error_band_vs_unquantised_oracle():
+    """Four e4m3-rounded operands: the recipe's error against the exact
+    attention on the bf16 inputs is a few percent (relative L2) with cosine
+    well above 0.99, and is zero-mean noise rather than a bias."""
+    (q, k, v), (q8, k8, v8, sq, sk, sv) = _quantized_inputs(1024, 18, H=2)
+    scale = 1.0 / math.sqrt(128)
+    o8, _ = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale)
+    ref, _ = oracle.attn(q, k, v, scale)
+    a, b = o8.ravel(), ref.ravel()
+    rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+    cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+    assert 0.02 <= rel <= 0.09, rel
+    assert cos >= 0.99
+    assert abs(np.mean(a - b)) <= 0.05 * np.sqrt(np.mean((a - b) ** 2))
