@@ -1,0 +1,147 @@
+/*
+ * dit_attn.h -- C ABI of the dit_attn library: non-causal joint attention
+ * forward for diffusion transformers on one AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  FLUX-family DiTs embed text tokens, noisy target-image
+ * latent tokens and an optional reference image separately and then unite
+ * them in one shared attention layer (bpdata.com "FLUX 3 Image Klein
+ * optimalizálása", section "Modellezés és pipeline jellemzők").  That layer
+ * is plain bidirectional softmax attention over the concatenated sequence:
+ *
+ *     O[b,h,i,:] = sum_j softmax_j(scale * <Q[b,h,i,:], K[b,h,j,:]>) V[b,h,j,:]
+ *
+ * with no causal mask.  The pages select among a "VANILLA" BF16 attention,
+ * quantised FP8 attention, and block-sparse attention backends (scopeai.cc
+ * page, section "各项优化的效果与质量代价"; bpdata.com page, section "Mi
+ * szerepel az optimalizálásban"); the three calls below are this library's
+ * versions of those three.
+ *
+ * Conventions shared by every call.
+ *  - Tensors.  Q, K, V and O are [B, H, N, D] with element strides given per
+ *    tensor for (b, h, n); the d stride is 1.  Q, K, V are bfloat16.  O is
+ *    bfloat16 (round to nearest even), or fp32 when DIT_ATTN_FLAG_OUT_F32 is
+ *    set.  D must be 128.
+ *  - Optional lse output: fp32 [B, H, N] contiguous, lse = ln sum_j
+ *    exp(scale * <q_i, k_j>) over the keys the row attends to.  Pass NULL to
+ *    skip it.  A row that attends to no key gets O = 0 and lse = -inf.
+ *  - Pointers are device pointers.  Q, K, V, O must be 16-byte aligned; every
+ *    (b, h, n) stride of Q, K, V and O must be a multiple of 8 elements.
+ *  - Ownership.  The caller owns every buffer and the stream; the library
+ *    never allocates or frees memory.
+ *  - Asynchrony.  Calls enqueue work on `stream` (a hipStream_t; NULL is the
+ *    default stream) and return without waiting; they never read device
+ *    memory from the host, so they may be captured into a HIP graph.
+ *  - Errors.  All arguments are checked before any HIP call; on a bad
+ *    argument nothing is launched and a nonzero dit_attn_status is returned.
+ *    dit_attn_last_error() then gives a per-thread description.
+ *  - Determinism.  For a fixed build, device and arguments the output is
+ *    bitwise reproducible: reductions use no atomics and a fixed key order.
+ *  - Thread safety.  Calls are re-entrant; there is no global mutable state
+ *    besides the per-thread error string.
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dit_attn_status {
+    DIT_ATTN_OK = 0,
+    DIT_ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size/stride/alignment */
+    DIT_ATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not cover (e.g. D != 128) */
+    DIT_ATTN_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
+    DIT_ATTN_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} dit_attn_status;
+
+/* Store O as fp32 instead of bfloat16 (the arithmetic is unchanged, so the
+ * bf16 output equals the round-to-nearest-even image of the fp32 output). */
+#define DIT_ATTN_FLAG_OUT_F32 1u
+
+/* Problem description.  Strides are in elements, for (b, h, n). */
+typedef struct dit_attn_shape {
+    int32_t batch;       /* B >= 1 */
+    int32_t heads;       /* H >= 1 */
+    int32_t seqlen;      /* N >= 1: text + image (+ reference) tokens */
+    int32_t head_dim;    /* D, must be 128 */
+    int64_t q_stride[3];
+    int64_t k_stride[3];
+    int64_t v_stride[3];
+    int64_t o_stride[3];
+    float softmax_scale; /* > 0 and finite; 1/sqrt(D) for the DiT workloads */
+    uint32_t flags;      /* DIT_ATTN_FLAG_* */
+} dit_attn_shape;
+
+/* Dense bf16 joint attention (the "VANILLA BF16 attention" backend).
+ * Flash-style: QK^T and PV on bf16 MFMA with fp32 accumulation, online
+ * softmax in fp32, P rounded to bf16 for the PV product. */
+int dit_attn_fwd(const dit_attn_shape* shape,
+                 const void* q, const void* k, const void* v,
+                 void* o, float* lse, void* stream);
+
+/* Workspace bytes dit_attn_fwd_fp8 / dit_attn_fp8_quantize need for `shape`
+ * (0 if the shape is invalid).  Layout, with BH = B*H, nb = ceil(N/128),
+ * Np = 128*nb, each region starting at a 256-byte boundary in this order:
+ *   Q8  uint8 [BH][Np][128]  e4m3 codes of Q, rows >= N are 0
+ *   K8  uint8 [BH][Np][128]  e4m3 codes of K, rows >= N are 0
+ *   V8t uint8 [BH][128][Np]  e4m3 codes of V transposed (d-major); within
+ *       every 64-key group the 4-key groups are stored in the order the PV
+ *       operand is read: position group pg holds key group
+ *       8*((pg>>2)&1) + 2*(pg&3) + (pg>>3); keys >= N are 0
+ *   sQ, sK, sV  fp32 [BH][nb]  dequantisation scales (absmax / 448) */
+size_t dit_attn_fwd_fp8_workspace_bytes(const dit_attn_shape* shape);
+
+/* Quantised attention with on-device dynamic scaling.  FP8 dynamic
+ * quantisation of activations (wavespeed.ai FLUX.1-dev page, section "FP8
+ * Dynamische Quantisierung") applied to attention: Q, K and V are quantised
+ * to OCP e4m3 with one scale per (b, h, 128-token block):
+ *     s = absmax / 448,  code = e4m3_rne(clamp(x * (448 / absmax), +-448))
+ * (absmax == 0 gives s = 1 and zero codes).  QK^T runs on fp8 MFMA; the
+ * online softmax keeps a running max per 128-key block; the unnormalised
+ * probabilities w in [0, 1] are quantised as e4m3(448 w) for the fp8 PV
+ * product; the row sum uses the unquantised w; output is bf16 (or fp32).
+ * The quantisation pass writes the workspace (layout above), then the
+ * attention pass reads it, both on `stream`. */
+int dit_attn_fwd_fp8(const dit_attn_shape* shape,
+                     const void* q, const void* k, const void* v,
+                     void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Only the quantisation pass of dit_attn_fwd_fp8: fills the workspace (same
+ * layout) so a caller can inspect or reuse the e4m3 codes and scales. */
+int dit_attn_fp8_quantize(const dit_attn_shape* shape,
+                          const void* q, const void* k, const void* v,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Block-sparse bf16 attention over 128x128 (query block, key block) tiles
+ * (the "blokksparse" attention backend, bpdata.com page, section "Mi
+ * szerepel az optimalizálásban").  block_mask is a device uint8 array
+ * [ceil(N/128)][ceil(N/128)], row = query block, column = key block, nonzero
+ * = attend.  Masked blocks act as -inf logits: they are skipped and their K
+ * and V are never read.  mask_stride_bh is the element offset between the
+ * masks of consecutive (b, h) slices (b-major); 0 shares one mask.
+ * block_size must be 128.  The arithmetic per kept block is identical to
+ * dit_attn_fwd, so an all-ones mask reproduces it bit for bit. */
+int dit_attn_fwd_blocksparse(const dit_attn_shape* shape,
+                             const void* q, const void* k, const void* v,
+                             void* o, float* lse,
+                             const uint8_t* block_mask, int64_t mask_stride_bh,
+                             int32_t block_size, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* dit_attn_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* dit_attn_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int dit_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */

@@ -1,0 +1,50 @@
+// launch.h -- internal interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+// Arguments of the bf16 attention kernels (dense and block-sparse).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;           // nullable, [B*H][N]
+  int64_t qs[3], ks[3], vs[3], os[3];  // element strides of (b, h, n)
+  uint32_t q_bytes, k_bytes, v_bytes;  // extent of one (b, h) slice in bytes
+  int B, H, N;
+  int nqb;              // query blocks per (b, h)
+  float c;              // softmax_scale * log2(e)
+  const uint8_t* mask;  // block-sparse only: [nb][nb] per (b, h)
+  int64_t mask_bh;      // element offset between (b, h) masks
+  int nb;               // ceil(N / 128)
+};
+
+// Arguments of the fp8 quantisation pass and the fp8 attention kernel.
+struct Fp8Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  uint32_t q_bytes, k_bytes, v_bytes;
+  int B, H, N, nb, np;  // np = 128 * nb
+  uint8_t* q8;          // [BH][np][128]
+  uint8_t* k8;          // [BH][np][128]
+  uint8_t* v8t;         // [BH][128][np], key-permuted per 64-key group
+  float* sq;            // [BH][nb]
+  float* sk;
+  float* sv;
+  float c;              // softmax_scale * log2(e)
+  float p_off;          // log2(448) rounded down: w * 448 = exp2(x + p_off)
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, bool out_f32, bool sparse, hipStream_t s);
+hipError_t launch_fp8_quantize(const Fp8Args& a, hipStream_t s);
+hipError_t launch_attn_fp8(const Fp8Args& a, bool out_f32, hipStream_t s);
+
+}  // namespace dit
