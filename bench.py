@@ -1,0 +1,234 @@
+"""Benchmark of the joint-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--legs all|none]
+
+A step is one dense bf16 joint-attention forward (QK^T, online softmax, PV,
+epilogue -- the whole hot path of dit_attn_fwd) over the 2048x2048-image DiT
+shape with its CFG pair: B=2, H=24, N=512 text + 16384 image = 16896 tokens,
+D=128, 1% of key rows x8 (inputs already resident in HBM).  `value` is the
+algorithmic TFLOP/s of that step (4 N^2 D flops per (b, h)).
+
+In the same run and on the same stream, timed the same way (W warm-ups, then
+K timed launches between HIP events), the other kernels of the path are
+reported as legs: the fp8 recipe (quantisation pass + fp8 attention) and the
+block-sparse kernel at the same 2048^2 shape with B=1, and the dense kernel at
+the 1024^2 shape.  The fp64 CPU oracle is timed on a bounded sample of rows
+of the same workload as the CPU baseline.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "joint-attention TFLOP/s at 2048² DiT shape (bf16, fp8); % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def _flops_dense(B, H, N, D=128):
+    return 4.0 * B * H * N * N * D
+
+
+def _time_launches(fn, steps, warmup, torch):
+    """Average ms per launch of fn() between HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "joint_attention_non_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key: str, sha: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _cpu_baseline(w, q, k, v, budget_s=15.0):
+    import oracle
+    from workloads import sample_rows
+    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    probe = sample_rows(w.batch, w.heads, w.seqlen, 64, seed=1)
+    t0 = time.perf_counter()
+    oracle.attn(qd, kd, vd, w.scale, rows=probe)
+    dt = time.perf_counter() - t0
+    n = int(max(64, min(200000, len(probe) * budget_s / max(dt, 1e-6))))
+    rows = sample_rows(w.batch, w.heads, w.seqlen, n, seed=2)
+    t0 = time.perf_counter()
+    oracle.attn(qd, kd, vd, w.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = len(rows) * 4.0 * w.seqlen * w.head_dim
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} random query rows of {w.name} (all {w.seqlen} keys each), "
+                      f"fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--legs", default="all", choices=["all", "none"],
+                    help="also time the fp8 and block-sparse kernels at the 2048^2 shape")
+    ap.add_argument("--img1024", action="store_true",
+                    help="also time the dense kernel at the 1024^2 shape (same kernel name as "
+                         "the headline, so keep it out of profiled runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the joint-attention kernel is measured on one "
+              "GPU's share; multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import joint_attention_non_amd as dit
+    from workloads import WORKLOADS, make_workload_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dit.load()
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # ---- headline: dense bf16 at 2048^2 with the CFG pair ----
+    w = WORKLOADS["img2048"]
+    log(f"[bench] generating {w.name} inputs")
+    q, k, v, _ = make_workload_inputs(w, seed=0)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    log(f"[bench] timing {w.name}: warmup {args.warmup}, steps {args.steps}")
+    torch.cuda.synchronize()
+    ms = _time_launches(lambda: dit.attn_fwd(qd, kd, vd, out=o), args.steps, args.warmup, torch)
+    flops = _flops_dense(w.batch, w.heads, w.seqlen, w.head_dim)
+    tflops = flops / (ms * 1e-3) / 1e12
+    sha = _source_sha("attn_bf16.hip", "device_common.h")
+    traffic = _traffic("attn_bf16_img2048", sha)
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "attn_bf16_kernel<4,2,false,false>",
+                "flops_per_launch": flops}
+    log(f"[bench] {w.name}: {ms:.3f} ms  {tflops:.1f} TFLOP/s  {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
+    del o
+
+    legs = {}
+    if args.legs == "all":
+        # fp8 recipe at 2048^2, B=1
+        wf = WORKLOADS["img2048_fp8"]
+        log(f"[bench] leg {wf.name}")
+        qf, kf, vf, _ = make_workload_inputs(wf, seed=0)
+        qf, kf, vf = (t.to(dev) for t in (qf, kf, vf))
+        of = torch.empty_like(qf)
+        ws = torch.empty(dit.fp8_workspace_bytes(qf), dtype=torch.uint8, device=dev)
+        ms_f = _time_launches(lambda: dit.attn_fwd_fp8(qf, kf, vf, workspace=ws, out=of),
+                              args.steps, args.warmup, torch)
+        ms_q = _time_launches(lambda: dit.fp8_quantize(qf, kf, vf, workspace=ws),
+                              args.steps, args.warmup, torch)
+        ms_a = ms_f - ms_q
+        ff = _flops_dense(wf.batch, wf.heads, wf.seqlen, wf.head_dim)
+        nbq = (wf.seqlen + 127) // 128
+        qbytes = (3 * qf.numel() * 2                                  # bf16 Q, K, V read
+                  + 3 * wf.batch * wf.heads * nbq * 128 * wf.head_dim  # e4m3 codes written
+                  + 3 * wf.batch * wf.heads * nbq * 4)                 # fp32 scales written
+        legs[wf.name] = {
+            "ms_total": round(ms_f, 4), "ms_quantize": round(ms_q, 4), "ms_attention": round(ms_a, 4),
+            "tflops_total": round(ff / (ms_f * 1e-3) / 1e12, 2),
+            "attention": {"bound": "mfma", "achieved": round(ff / (ms_a * 1e-3) / 1e12, 2),
+                          "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(ff / (ms_a * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)},
+            "quantize": {"bound": "hbm", "achieved": round(qbytes / (ms_q * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(qbytes / (ms_q * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "bytes_per_launch": qbytes},
+        }
+        log(f"[bench] {wf.name}: {legs[wf.name]}")
+        del qf, kf, vf, of, ws
+
+        # block-sparse at 2048^2, B=1
+        wsp = WORKLOADS["img2048_sparse"]
+        log(f"[bench] leg {wsp.name}")
+        qs, ks, vs, mask = make_workload_inputs(wsp, seed=0)
+        active = int(mask.sum())
+        qs, ks, vs, md = (t.to(dev) for t in (qs, ks, vs, mask))
+        os_ = torch.empty_like(qs)
+        ms_s = _time_launches(lambda: dit.attn_fwd_blocksparse(qs, ks, vs, md, out=os_),
+                              args.steps, args.warmup, torch)
+        fs = 4.0 * wsp.batch * wsp.heads * active * 128 * 128 * wsp.head_dim
+        legs[wsp.name] = {"ms": round(ms_s, 4), "active_blocks": active,
+                          "total_blocks": int(mask.numel()),
+                          "bound": "mfma", "achieved": round(fs / (ms_s * 1e-3) / 1e12, 2),
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(fs / (ms_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "flops_counted": "active 128x128 blocks only"}
+        log(f"[bench] {wsp.name}: {legs[wsp.name]}")
+        del qs, ks, vs, md, os_
+
+    if args.img1024:
+        w1 = WORKLOADS["img1024"]
+        q1, k1, v1, _ = make_workload_inputs(w1, seed=0)
+        q1, k1, v1 = (t.to(dev) for t in (q1, k1, v1))
+        o1 = torch.empty_like(q1)
+        ms_1 = _time_launches(lambda: dit.attn_fwd(q1, k1, v1, out=o1), max(args.steps, 50),
+                              args.warmup, torch)
+        f1 = _flops_dense(w1.batch, w1.heads, w1.seqlen, w1.head_dim)
+        legs[w1.name] = {"ms": round(ms_1, 4), "achieved": round(f1 / (ms_1 * 1e-3) / 1e12, 2),
+                         "unit": "TFLOP/s", "frac": round(f1 / (ms_1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] {w1.name}: {legs[w1.name]}")
+        del q1, k1, v1, o1
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline (bounded sample)")
+        cpu = _cpu_baseline(w, q, k, v)
+        log(f"[bench] cpu: {cpu}")
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(w.describe(), softmax_scale="1/sqrt(128)", seed=0),
+        "roofline": roofline, "cpu_baseline": cpu, "legs": legs,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

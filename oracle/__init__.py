@@ -102,12 +102,17 @@ def attn(q, k, v, scale: float, mask=None, mask_stride_bh: int = 0, block: int =
     [B, H, N] (or [len(rows)]).  ``mask`` is uint8 [nb, nb] (shared by all
     (b, h) when mask_stride_bh == 0) or [B*H, nb, nb] with stride nb*nb."""
     qd, kd, vd = _as_f64(q), _as_f64(k), _as_f64(v)
+    if qd.ndim != 4 or kd.shape != qd.shape or vd.shape != qd.shape:
+        raise ValueError("q, k, v must all be [B, H, N, D] of one shape")
     B, H, N, D = qd.shape
     BH = B * H
     m = None
     if mask is not None:
         m = np.ascontiguousarray(np.asarray(mask.cpu() if hasattr(mask, "cpu") else mask,
                                             dtype=np.uint8))
+        nb = (N + block - 1) // block
+        if m.size < mask_stride_bh * (BH - 1) + nb * nb:
+            raise ValueError("mask is smaller than the (b, h) slices it must cover")
     r = None
     if rows is not None:
         r = np.ascontiguousarray(np.asarray(rows.cpu() if hasattr(rows, "cpu") else rows,
@@ -163,7 +168,13 @@ def attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale: float, quantize_p: bool = Tru
     """The fp8 recipe on oracle-quantised codes; returns (o, lse) like ``attn``."""
     q8, k8, v8 = (np.ascontiguousarray(a, dtype=np.uint8) for a in (q8, k8, v8))
     sq, sk, sv = (np.ascontiguousarray(a, dtype=np.float32) for a in (sq, sk, sv))
+    if q8.ndim != 4 or k8.shape != q8.shape or v8.shape != q8.shape:
+        raise ValueError("q8, k8, v8 must all be [B, H, N, D] of one shape")
     B, H, N, D = q8.shape
+    nb = (N + block - 1) // block
+    for s_ in (sq, sk, sv):
+        if s_.shape != (B, H, nb):
+            raise ValueError("scales must be [B, H, ceil(N / block)]")
     BH = B * H
     r = None
     if rows is not None:

@@ -1,0 +1,137 @@
+"""GPU parity of the block-sparse path against the fp64 oracle with the same
+128x128 block mask, plus the properties that tie it to the dense path."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import joint_attention_non_amd as dit
+import oracle
+from tests._metrics import (BF16_MAX_ABS, BF16_MEAN_ABS, bf16_elementwise_ok, errors,
+                            rne_bf16, to64)
+from workloads import WORKLOADS, make_block_mask, make_qkv, make_workload_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("N", [100, 128, 320, 700, 1100])
+def test_random_mask_full_parity(N):
+    _say(f"case: sparse N={N} B=1 H=2")
+    q, k, v = make_qkv(1, 2, N, 128, seed=70 + N)
+    mask = make_block_mask(N, 64, 0.3, seed=N)
+    o32, lse = dit.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), mask.to(DEV),
+                                        out_fp32=True, return_lse=True)
+    o16 = dit.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), mask.to(DEV))
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attn(q, k, v, 1.0 / math.sqrt(128), mask=mask)
+    e = errors(o32, ref)
+    assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
+    assert torch.equal(rne_bf16(o32).view(torch.int16), o16.view(torch.int16))
+    assert bf16_elementwise_ok(o16, ref).all()
+    assert np.max(np.abs(to64(lse) - ref_lse)) <= 1e-4
+
+
+def test_all_ones_mask_equals_dense_bitwise():
+    _say("case: all-ones mask vs dense")
+    for N in (320, 1000):
+        q, k, v = (t.to(DEV) for t in make_qkv(1, 3, N, 128, seed=80 + N))
+        nb = (N + 127) // 128
+        ones = torch.ones((nb, nb), dtype=torch.uint8, device=DEV)
+        o_s, l_s = dit.attn_fwd_blocksparse(q, k, v, ones, return_lse=True)
+        o_d, l_d = dit.attn_fwd(q, k, v, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o_s.view(torch.int16), o_d.view(torch.int16))
+        assert torch.equal(l_s, l_d)
+
+
+def test_diagonal_mask_is_segment_attention():
+    """Only diagonal blocks kept: each 128-token segment attends to itself,
+    which is the dense oracle run on that segment alone."""
+    _say("case: diagonal mask")
+    N = 400
+    q, k, v = make_qkv(1, 2, N, 128, seed=90)
+    nb = 4
+    mask = torch.eye(nb, dtype=torch.uint8)
+    o = dit.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), mask.to(DEV), out_fp32=True)
+    torch.cuda.synchronize()
+    for s in range(nb):
+        a, b = s * 128, min(N, (s + 1) * 128)
+        ref, _ = oracle.attn(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], 1.0 / math.sqrt(128))
+        e = errors(o[:, :, a:b], ref)
+        assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS
+
+
+def test_masked_blocks_are_never_read():
+    """Fill a key block that every query masks out with NaN: the output must
+    be finite, equal the oracle on the clean inputs with the same mask, and
+    match the kernel's own clean-input result bit for bit."""
+    _say("case: NaN-poisoned masked block")
+    N = 512
+    q, k, v = make_qkv(1, 2, N, 128, seed=91)
+    mask = torch.ones((4, 4), dtype=torch.uint8)
+    mask[:, 2] = 0
+    kp, vp = k.clone(), v.clone()
+    kp[:, :, 256:384] = float("nan")
+    vp[:, :, 256:384] = float("nan")
+    md = mask.to(DEV)
+    o = dit.attn_fwd_blocksparse(q.to(DEV), kp.to(DEV), vp.to(DEV), md, out_fp32=True)
+    o_clean = dit.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), md, out_fp32=True)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())
+    assert torch.equal(o, o_clean)
+    ref, _ = oracle.attn(q, k, v, 1.0 / math.sqrt(128), mask=mask)
+    e = errors(o, ref)
+    assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
+
+
+def test_fully_masked_row_gives_zero_and_neg_inf_lse():
+    _say("case: empty mask row")
+    N = 300
+    q, k, v = make_qkv(1, 1, N, 128, seed=92)
+    mask = torch.ones((3, 3), dtype=torch.uint8)
+    mask[1] = 0
+    o, lse = dit.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), mask.to(DEV),
+                                      out_fp32=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert float(o[0, 0, 128:256].abs().max()) == 0.0
+    assert bool(torch.isneginf(lse[0, 0, 128:256]).all())
+    ref, _ = oracle.attn(q, k, v, 1.0 / math.sqrt(128), mask=mask)
+    e = errors(o, ref)
+    assert e["max_abs"] <= BF16_MAX_ABS
+
+
+def test_per_head_masks():
+    _say("case: per-(b,h) masks")
+    N = 384
+    q, k, v = make_qkv(1, 3, N, 128, seed=93)
+    masks = torch.stack([make_block_mask(N, 0, 0.4, seed=s) for s in range(3)])
+    o = dit.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), masks.to(DEV), out_fp32=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle.attn(q, k, v, 1.0 / math.sqrt(128), mask=masks, mask_stride_bh=9)
+    e = errors(o, ref)
+    assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
+
+
+def test_img2048_sparse_sampled_parity():
+    w = WORKLOADS["img2048_sparse"]
+    _say(f"case: {w.describe()} sampled")
+    q, k, v, mask = make_workload_inputs(w, seed=0)
+    _say(f"active blocks: {int(mask.sum())} of {mask.numel()}")
+    qd, kd, vd, md = (t.to(DEV) for t in (q, k, v, mask))
+    o32 = dit.attn_fwd_blocksparse(qd, kd, vd, md, out_fp32=True)
+    o16 = dit.attn_fwd_blocksparse(qd, kd, vd, md)
+    torch.cuda.synchronize()
+    assert torch.equal(rne_bf16(o32).view(torch.int16), o16.view(torch.int16))
+    rows = sample_rows(w.batch, w.heads, w.seqlen, 384, seed=0)
+    ref, _ = oracle.attn(q, k, v, w.scale, mask=mask, rows=rows)
+    got = o32.reshape(-1, 128)[rows.to(DEV)].cpu()
+    e = errors(got, ref)
+    _say(f"sparse fp32-out {e}")
+    assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
+    assert bf16_elementwise_ok(o16.reshape(-1, 128)[rows.to(DEV)].cpu(), ref).all()
