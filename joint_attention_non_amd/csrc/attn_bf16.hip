@@ -11,9 +11,11 @@
 //                    transposed product each lane holds 16 keys of one query
 //                    row, so the row max and row sum are in-register
 //                    reductions plus one exchange with lane l^32.
-//   online softmax   m' = max(m, rowmax S); alpha = 2^((m - m') c);
-//                    P = 2^(S c - m' c) with c = scale * log2(e);
-//                    l = alpha l + sum P; O *= alpha.
+//   online softmax   P = 2^(S c - m c) with c = scale * log2(e) and m the
+//                    running row max; l += sum P.  m is only moved when a
+//                    row's max grows by more than 2^8 in P units: then
+//                    alpha = 2^((m - m') c), O *= alpha, l *= alpha.  The
+//                    result is the same softmax (the factor cancels in O / l).
 //   O^T += V^T P^T   A = V^T from LDS, B = P straight from the S registers
 //                    rounded to bf16 -- no shuffle: the PV reduction index
 //                    is permuted instead, by storing the V^T tile in LDS with
@@ -35,6 +37,9 @@ constexpr int D = kHeadDim;
 constexpr int BN = 64;        // keys per LDS tile
 constexpr int KS = D + 8;     // K tile row stride in bf16 (272 B: conflict-free b128 reads)
 constexpr int VS = BN + 8;    // V^T tile row stride in bf16 (144 B)
+// Lazy rescaling: P = 2^(S c - m c) may reach 2^kLazy before the running max
+// m is moved, so O and l are rescaled only on large jumps of the row max.
+constexpr float kLazy = 8.f;
 
 // Position (in 4-key groups) of key group g4 inside a 16-key group of the
 // V^T tile.  Lane half h of the PV operand reads 8 consecutive keys at 8h:
@@ -180,10 +185,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qi][db][r] = 0.f;
-  float m_run[R], l_run[R];
+  // m_run: running max of the raw dot products (the value P is taken
+  // against), mc_run = m_run * c (0 until the first tile sets it).
+  float m_run[R], mc_run[R], l_run[R];
 #pragma unroll
   for (int qi = 0; qi < R; ++qi) {
     m_run[qi] = -INFINITY;
+    mc_run[qi] = 0.f;
     l_run[qi] = 0.f;
   }
 
@@ -210,12 +218,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
   if (k_nxt >= 0) ld.load(rk, rv, krow, vrow, k_nxt, tid);
   __syncthreads();
 
-  int buf = 0;
-  while (k_cur >= 0) {
-    const __bf16* sK = smK[buf];
-    const __bf16* sV = smV[buf];
-
-    // ---- S^T = K Q^T (raw dot products) ----
+  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK is set
+  // only for the ragged last tile, so full tiles carry no key compares.
+  auto tile_body = [&](auto mask_tag, const __bf16* sK, const __bf16* sV, int k_cur) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 sacc[R][2];
 #pragma unroll
     for (int qi = 0; qi < R; ++qi)
@@ -234,8 +240,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
       }
     }
 
-    // ---- keys past N in the ragged last tile get -inf ----
-    if (k_cur + BN > N) {
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -248,39 +253,57 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
         }
     }
 
-    // ---- online softmax ----
-    uint32_t pk[R][2][8];   // P as packed bf16 pairs, [qi][kb][pair]
+    // Row max of the tile; the running max moves (and O, l are rescaled)
+    // only when some row of the wave gains more than 2^kLazy, so most
+    // tiles skip the rescale of the 64 x 128 accumulator.
+    float mx[R];
+    bool grow = false;
 #pragma unroll
     for (int qi = 0; qi < R; ++qi) {
-      float mx = m_run[qi];
+      float t = sacc[qi][0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qi][kb][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const bool empty = (mx == -INFINITY);
-      const float alpha = empty ? 1.f : fast_exp2((m_run[qi] - mx) * c);
-      const float mc = empty ? 0.f : mx * c;
-      float ls = 0.f;
+        for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[qi][kb][r]);
+      t = fmaxf(t, swap_halves(t));
+      mx[qi] = t;
+      grow |= (t - m_run[qi]) * c > kLazy;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int qi = 0; qi < R; ++qi) {
+        const float mnew = fmaxf(m_run[qi], mx[qi]);
+        const float alpha = fast_exp2((m_run[qi] - mnew) * c);
+        l_run[qi] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qi][db][r] *= alpha;
+        m_run[qi] = mnew;
+        mc_run[qi] = mnew * c;
+      }
+    }
+
+    // P rounded to bf16 (round to nearest even) feeds the PV product, and the
+    // row sum is taken over those same rounded weights (one v_dot2 with
+    // (1, 1) per pair), so the normalised weights stay a convex combination
+    // even when a single key dominates the row.
+    uint32_t pk[R][2][8];   // P as packed bf16 pairs, [qi][kb][pair]
+#pragma unroll
+    for (int qi = 0; qi < R; ++qi) {
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(sacc[qi][kb][r], c, -mc));
-          const float p1 = fast_exp2(__builtin_fmaf(sacc[qi][kb][r + 1], c, -mc));
-          ls += p0;
-          ls += p1;
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[qi][kb][r], c, -mc_run[qi]));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[qi][kb][r + 1], c, -mc_run[qi]));
           pk[qi][kb][r >> 1] = pack_bf16x2(p0, p1);
+          ls[(r >> 1) & 3] = sum_bf16x2(pk[qi][kb][r >> 1], ls[(r >> 1) & 3]);
         }
-      l_run[qi] = l_run[qi] * alpha + ls;
-      m_run[qi] = mx;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[qi][db][r] *= alpha;
+      l_run[qi] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
 
-    // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       bf16x8 pf[R];
@@ -299,6 +322,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
           oacc[qi][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qi], oacc[qi][db], 0, 0, 0);
       }
     }
+  };
+
+  // Full tiles; the ragged tile (if any) holds key N - 1 and so comes last
+  // in both the dense and the block-sparse order: it runs after the loop.
+  int buf = 0;
+  while (k_cur >= 0 && k_cur + BN <= N) {
+    tile_body(std::false_type{}, smK[buf], smV[buf], k_cur);
 
     int k_nn = -1;
     if (k_nxt >= 0) {
@@ -311,6 +341,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     k_nxt = k_nn;
     buf ^= 1;
   }
+  if (k_cur >= 0) tile_body(std::true_type{}, smK[buf], smV[buf], k_cur);
 
   // ---- epilogue ----
   const int64_t ob = b * a.os[0] + hd * a.os[1];

@@ -10,6 +10,10 @@ Tolerances (stated once here, used by every parity test):
   bit, and element-wise to lie within 1e-2, or within half a bf16 step of the
   oracle value plus 1e-3 where the value is so large that bf16 rounding alone
   exceeds 1e-2 (|O| >= 2: a bf16 step there is 2^-6 or more).
+* lse (bf16 paths): the kernel normalises by the sum of the bf16-rounded
+  weights it multiplies V with; each weight carries a relative rounding
+  error of at most 2^-8 (bf16 unit roundoff, 8 significant bits), so
+  ln(sum) moves by at most ln(1 + 2^-8) < 2^-8.
 * fp8 path: cosine >= 0.99 and relative L2 <= 5e-2 against the oracle on the
   unquantised inputs; against the oracle's fp8 recipe (same codes, same
   running-max blocks) relative L2 <= 5e-3.
@@ -19,6 +23,7 @@ import torch
 
 BF16_MAX_ABS = 1e-2
 BF16_MEAN_ABS = 1e-3
+LSE_ABS = 2.0 ** -8 + 1e-5
 FP8_COS = 0.99
 FP8_REL_L2 = 5e-2
 FP8_RECIPE_REL_L2 = 5e-3

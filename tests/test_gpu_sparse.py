@@ -8,7 +8,7 @@ import torch
 
 import joint_attention_non_amd as dit
 import oracle
-from tests._metrics import (BF16_MAX_ABS, BF16_MEAN_ABS, bf16_elementwise_ok, errors,
+from tests._metrics import (BF16_MAX_ABS, BF16_MEAN_ABS, LSE_ABS, bf16_elementwise_ok, errors,
                             rne_bf16, to64)
 from workloads import WORKLOADS, make_block_mask, make_qkv, make_workload_inputs, sample_rows
 
@@ -34,7 +34,7 @@ def test_random_mask_full_parity(N):
     assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
     assert torch.equal(rne_bf16(o32).view(torch.int16), o16.view(torch.int16))
     assert bf16_elementwise_ok(o16, ref).all()
-    assert np.max(np.abs(to64(lse) - ref_lse)) <= 1e-4
+    assert np.max(np.abs(to64(lse) - ref_lse)) <= LSE_ABS
 
 
 def test_all_ones_mask_equals_dense_bitwise():
