@@ -47,53 +47,75 @@ constexpr float kLazy = 8.f;
 // {4..7, 12..15} of every 16, so groups 1 and 2 trade places.
 __device__ __forceinline__ int vpos16(int g4) { return ((g4 & 1) << 1) | (g4 >> 1); }
 
+// Global -> register -> LDS staging of one K tile (row-major, padded rows)
+// and one V^T tile (d-major, keys permuted per 16 as above).  K moves as
+// 16-byte chunks; V as units of 4 keys x 8 d that are transposed in
+// registers (16 v_perm-style ops) and written as 8-byte rows of V^T.  With
+// 512 threads the first half of the work-group moves V and the second K.
 template <int NT>
 struct TileLoader {
-  static constexpr int KCH = BN * (D / 8) / NT;         // 16-byte K chunks per thread
-  static constexpr int VUN = (BN / 4) * (D / 8) / NT;   // 4-key x 8-d V units per thread
-  static_assert(KCH * NT == BN * (D / 8) && VUN * NT == (BN / 4) * (D / 8), "tile split");
+  static constexpr int KCHUNKS = BN * (D / 8);        // 16-byte K chunks per tile
+  static constexpr int VUNITS = (BN / 4) * (D / 8);   // V units per tile
+  static constexpr bool SPLIT = NT > VUNITS;          // separate K and V threads
+  static constexpr int KCH = SPLIT ? KCHUNKS / (NT - VUNITS) : KCHUNKS / NT;
+  static constexpr int VUN = SPLIT ? 1 : VUNITS / NT;
+  static_assert(SPLIT ? (KCH * (NT - VUNITS) == KCHUNKS && NT - VUNITS > 0)
+                      : (KCH * NT == KCHUNKS && VUN * NT == VUNITS), "tile split");
   u32x4 kr[KCH];
   u32x4 vr[VUN][4];
 
+  __device__ __forceinline__ bool does_k(int tid) const { return !SPLIT || tid >= VUNITS; }
+  __device__ __forceinline__ bool does_v(int tid) const { return !SPLIT || tid < VUNITS; }
+  __device__ __forceinline__ int ktid(int tid) const { return SPLIT ? tid - VUNITS : tid; }
+  static constexpr int KSTRIDE = SPLIT ? NT - VUNITS : NT;
+
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                        uint32_t krow, uint32_t vrow, int key0, int tid) {
+    if (does_k(tid)) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + i * NT, key = id >> 4, c = id & 15;
-      kr[i] = buf_load_b128(rk, (uint32_t)(key0 + key) * krow + c * 16);
+      for (int i = 0; i < KCH; ++i) {
+        const int id = ktid(tid) + i * KSTRIDE, key = id >> 4, c = id & 15;
+        kr[i] = buf_load_b128(rk, (uint32_t)(key0 + key) * krow + c * 16);
+      }
     }
+    if (does_v(tid)) {
 #pragma unroll
-    for (int u = 0; u < VUN; ++u) {
-      const int id = tid + u * NT, g = id & 15, c = id >> 4;
+      for (int u = 0; u < VUN; ++u) {
+        const int id = tid + u * NT, g = id & 15, c = id >> 4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vr[u][r] = buf_load_b128(rv, (uint32_t)(key0 + 4 * g + r) * vrow + c * 16);
+        for (int r = 0; r < 4; ++r)
+          vr[u][r] = buf_load_b128(rv, (uint32_t)(key0 + 4 * g + r) * vrow + c * 16);
+      }
     }
   }
 
   __device__ __forceinline__ void store(__bf16* sk, __bf16* sv, int tid) const {
+    if (does_k(tid)) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + i * NT, key = id >> 4, c = id & 15;
-      *reinterpret_cast<u32x4*>(sk + key * KS + c * 8) = kr[i];
+      for (int i = 0; i < KCH; ++i) {
+        const int id = ktid(tid) + i * KSTRIDE, key = id >> 4, c = id & 15;
+        *reinterpret_cast<u32x4*>(sk + key * KS + c * 8) = kr[i];
+      }
     }
+    if (does_v(tid)) {
 #pragma unroll
-    for (int u = 0; u < VUN; ++u) {
-      const int id = tid + u * NT, g = id & 15, c = id >> 4;
-      const int pos = 16 * (g >> 2) + 4 * vpos16(g & 3);
+      for (int u = 0; u < VUN; ++u) {
+        const int id = tid + u * NT, g = id & 15, c = id >> 4;
+        const int pos = 16 * (g >> 2) + 4 * vpos16(g & 3);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int w = j >> 1;
-        const uint32_t a0 = vr[u][0][w], a1 = vr[u][1][w], a2 = vr[u][2][w], a3 = vr[u][3][w];
-        u32x2 out;
-        if ((j & 1) == 0) {
-          out[0] = (a0 & 0xffffu) | (a1 << 16);
-          out[1] = (a2 & 0xffffu) | (a3 << 16);
-        } else {
-          out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-          out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+        for (int j = 0; j < 8; ++j) {
+          const int w = j >> 1;
+          const uint32_t a0 = vr[u][0][w], a1 = vr[u][1][w], a2 = vr[u][2][w], a3 = vr[u][3][w];
+          u32x2 out;
+          if ((j & 1) == 0) {
+            out[0] = (a0 & 0xffffu) | (a1 << 16);
+            out[1] = (a2 & 0xffffu) | (a3 << 16);
+          } else {
+            out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+            out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+          }
+          *reinterpret_cast<u32x2*>(sv + (8 * c + j) * VS + pos) = out;
         }
-        *reinterpret_cast<u32x2*>(sv + (8 * c + j) * VS + pos) = out;
       }
     }
   }
@@ -142,7 +164,7 @@ struct SparseTiles {
 };
 
 template <int NW, int R, bool OUT_F32, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32 * R;
   static_assert(!SPARSE || BM == kBlock, "block-sparse work-groups cover one 128-row mask block");
@@ -386,8 +408,8 @@ hipError_t launch_attn_bf16(const AttnArgs& args, bool out_f32, bool sparse, hip
     if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<4, 1, true, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((attn_bf16_kernel<4, 1, false, true>), grid, dim3(256), 0, s, a);
   } else {
-    if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<4, 2, true, false>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<4, 2, false, false>), grid, dim3(256), 0, s, a);
+    if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<8, 1, true, false>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<8, 1, false, false>), grid, dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }
