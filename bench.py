@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--legs", default="all", choices=["all", "none"],
                     help="also time the fp8 and block-sparse kernels at the 2048^2 shape")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run one device-to-device copy of MIB MiB (a kernel of "
+                         "known traffic, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--img1024", action="store_true",
                     help="also time the dense kernel at the 1024^2 shape (same kernel name as "
                          "the headline, so keep it out of profiled runs)")
@@ -142,7 +145,7 @@ def main():
     traffic = _traffic("attn_bf16_img2048", sha)
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "attn_bf16_kernel<4,2,false,false>",
+                "traffic": traffic, "kernel": "attn_bf16_kernel<8,false,false>",
                 "flops_per_launch": flops}
     log(f"[bench] {w.name}: {ms:.3f} ms  {tflops:.1f} TFLOP/s  {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
     del o
@@ -211,6 +214,16 @@ def main():
                          "unit": "TFLOP/s", "frac": round(f1 / (ms_1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         log(f"[bench] {w1.name}: {legs[w1.name]}")
         del q1, k1, v1, o1
+
+    if args.calib_copy:
+        n = args.calib_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {args.calib_copy} MiB read + {args.calib_copy} MiB written")
+        del src, dst
 
     cpu = None
     if not args.no_cpu:

@@ -1,10 +1,9 @@
 // attn_bf16.hip -- bf16 flash-style joint attention forward for gfx950.
 //
-// One work-group owns BM = 32 * R * NW query rows of one (batch, head); each
-// wave owns R blocks of 32 rows (R = 2 dense: 256 rows per work-group; R = 1
-// block-sparse: 128 rows, one mask row).  K and V stream through LDS in
-// tiles of 64 keys, double-buffered: the global loads of tile t+2 are in
-// flight while tile t is computed and tile t+1 waits in the other LDS buffer.
+// A work-group of NW waves owns 32 * NW query rows of one (batch, head); each
+// wave owns 32 rows.  K and V stream through LDS in tiles of 64 keys, in
+// three rotating buffers: while tile t is finished, tile t+1 is already in
+// LDS and tile t+2 is being stored from registers loaded one step earlier.
 //
 // Per tile and wave, with the 32x32x16 bf16 MFMA (fp32 accumulate):
 //   S^T = K Q^T      A = K rows from LDS, B = Q held in registers.  In the
@@ -12,14 +11,23 @@
 //                    row, so the row max and row sum are in-register
 //                    reductions plus one exchange with lane l^32.
 //   online softmax   P = 2^(S c - m c) with c = scale * log2(e) and m the
-//                    running row max; l += sum P.  m is only moved when a
-//                    row's max grows by more than 2^8 in P units: then
+//                    running row max.  m is only moved when a row's max
+//                    grows by more than 2^8 in P units: then
 //                    alpha = 2^((m - m') c), O *= alpha, l *= alpha.  The
-//                    result is the same softmax (the factor cancels in O / l).
-//   O^T += V^T P^T   A = V^T from LDS, B = P straight from the S registers
-//                    rounded to bf16 -- no shuffle: the PV reduction index
-//                    is permuted instead, by storing the V^T tile in LDS with
-//                    its keys in the order the accumulator hands P out.
+//                    factor cancels in O / l, so the result is unchanged.
+//   O^T += V^T P^T   A = V^T, read from the row-major V tile with the gfx950
+//                    transposing LDS read (ds_read_b64_tr_b16: 16 lanes
+//                    fetch a 4-key x 16-d block and each lane receives one d
+//                    column of it), B = P straight from the S registers
+//                    rounded to bf16 -- no shuffle: the PV reduction index is
+//                    permuted instead, by choosing which 4 keys each
+//                    transposing read fetches to match the order in which
+//                    the accumulator hands P out.  l accumulates the same
+//                    rounded P (v_dot2 with (1, 1)).
+// Software pipeline: step t issues the QK^T MFMAs of tile t+1 interleaved
+// with the softmax VALU work of tile t, then the PV MFMAs of tile t
+// interleaved with the LDS stores of tile t+2 and the global loads of tile
+// t+3, so the matrix cores and the vector ALUs work at the same time.
 // Epilogue: O = O^T / l, stored bf16 (round to nearest even) or fp32, and
 // optionally lse = ln2 * (m c + log2 l).
 //
@@ -36,90 +44,63 @@ namespace {
 constexpr int D = kHeadDim;
 constexpr int BN = 64;        // keys per LDS tile
 constexpr int KS = D + 8;     // K tile row stride in bf16 (272 B: conflict-free b128 reads)
-constexpr int VS = BN + 8;    // V^T tile row stride in bf16 (144 B)
+constexpr int VSR = D + 32;   // V tile row stride in bf16 (320 B: 4 consecutive rows of a
+                              // transposing read land in disjoint bank quarters)
 // Lazy rescaling: P = 2^(S c - m c) may reach 2^kLazy before the running max
 // m is moved, so O and l are rescaled only on large jumps of the row max.
 constexpr float kLazy = 8.f;
 
-// Position (in 4-key groups) of key group g4 inside a 16-key group of the
-// V^T tile.  Lane half h of the PV operand reads 8 consecutive keys at 8h:
-// the 32x32 accumulator gives half 0 keys {0..3, 8..11} and half 1 keys
-// {4..7, 12..15} of every 16, so groups 1 and 2 trade places.
-__device__ __forceinline__ int vpos16(int g4) { return ((g4 & 1) << 1) | (g4 >> 1); }
-
-// Global -> register -> LDS staging of one K tile (row-major, padded rows)
-// and one V^T tile (d-major, keys permuted per 16 as above).  K moves as
-// 16-byte chunks; V as units of 4 keys x 8 d that are transposed in
-// registers (16 v_perm-style ops) and written as 8-byte rows of V^T.  With
-// 512 threads the first half of the work-group moves V and the second K.
+// Global -> register -> LDS staging of one tile: K and V both row-major
+// (padded rows), moved as 16-byte chunks; the tile's 2048 chunks are dealt
+// round-robin over the work-group, K first.
 template <int NT>
 struct TileLoader {
-  static constexpr int KCHUNKS = BN * (D / 8);        // 16-byte K chunks per tile
-  static constexpr int VUNITS = (BN / 4) * (D / 8);   // V units per tile
-  static constexpr bool SPLIT = NT > VUNITS;          // separate K and V threads
-  static constexpr int KCH = SPLIT ? KCHUNKS / (NT - VUNITS) : KCHUNKS / NT;
-  static constexpr int VUN = SPLIT ? 1 : VUNITS / NT;
-  static_assert(SPLIT ? (KCH * (NT - VUNITS) == KCHUNKS && NT - VUNITS > 0)
-                      : (KCH * NT == KCHUNKS && VUN * NT == VUNITS), "tile split");
-  u32x4 kr[KCH];
-  u32x4 vr[VUN][4];
-
-  __device__ __forceinline__ bool does_k(int tid) const { return !SPLIT || tid >= VUNITS; }
-  __device__ __forceinline__ bool does_v(int tid) const { return !SPLIT || tid < VUNITS; }
-  __device__ __forceinline__ int ktid(int tid) const { return SPLIT ? tid - VUNITS : tid; }
-  static constexpr int KSTRIDE = SPLIT ? NT - VUNITS : NT;
+  static constexpr int CHUNKS = 2 * BN * (D / 8);
+  static constexpr int CH = CHUNKS / NT;
+  static_assert(CH * NT == CHUNKS && (BN * (D / 8)) % NT == 0, "tile split");
+  u32x4 r[CH];
 
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                        uint32_t krow, uint32_t vrow, int key0, int tid) {
-    if (does_k(tid)) {
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int id = ktid(tid) + i * KSTRIDE, key = id >> 4, c = id & 15;
-        kr[i] = buf_load_b128(rk, (uint32_t)(key0 + key) * krow + c * 16);
-      }
-    }
-    if (does_v(tid)) {
-#pragma unroll
-      for (int u = 0; u < VUN; ++u) {
-        const int id = tid + u * NT, g = id & 15, c = id >> 4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vr[u][r] = buf_load_b128(rv, (uint32_t)(key0 + 4 * g + r) * vrow + c * 16);
-      }
+    for (int i = 0; i < CH; ++i) {
+      const int id = tid + i * NT;
+      const bool isk = id < BN * (D / 8);            // compile-time per i
+      const int cid = isk ? id : id - BN * (D / 8), key = cid >> 4, c = cid & 15;
+      r[i] = buf_load_b128(isk ? rk : rv, (uint32_t)(key0 + key) * (isk ? krow : vrow) + c * 16);
     }
   }
 
   __device__ __forceinline__ void store(__bf16* sk, __bf16* sv, int tid) const {
-    if (does_k(tid)) {
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int id = ktid(tid) + i * KSTRIDE, key = id >> 4, c = id & 15;
-        *reinterpret_cast<u32x4*>(sk + key * KS + c * 8) = kr[i];
-      }
-    }
-    if (does_v(tid)) {
-#pragma unroll
-      for (int u = 0; u < VUN; ++u) {
-        const int id = tid + u * NT, g = id & 15, c = id >> 4;
-        const int pos = 16 * (g >> 2) + 4 * vpos16(g & 3);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int w = j >> 1;
-          const uint32_t a0 = vr[u][0][w], a1 = vr[u][1][w], a2 = vr[u][2][w], a3 = vr[u][3][w];
-          u32x2 out;
-          if ((j & 1) == 0) {
-            out[0] = (a0 & 0xffffu) | (a1 << 16);
-            out[1] = (a2 & 0xffffu) | (a3 << 16);
-          } else {
-            out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-            out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-          }
-          *reinterpret_cast<u32x2*>(sv + (8 * c + j) * VS + pos) = out;
-        }
-      }
+    for (int i = 0; i < CH; ++i) {
+      const int id = tid + i * NT;
+      const bool isk = id < BN * (D / 8);
+      const int cid = isk ? id : id - BN * (D / 8), key = cid >> 4, c = cid & 15;
+      *reinterpret_cast<u32x4*>((isk ? sk + key * KS : sv + key * VSR) + c * 8) = r[i];
     }
   }
 };
+
+// A operand of O^T += V^T P^T for k-step s4 (16 keys) and d block db: lane
+// (l32, h) needs V[key][32 db + l32] for the 8 keys its P registers cover,
+// keys 16 s4 + 8 r + 4 h + j (r, j = 0..3).  Each transposing read serves
+// one r: lane s of a 16-lane group points at row 16 s4 + 8 r + 4 h + s/4,
+// columns 32 db + 16 (group & 1) + 4 (s & 3) .. +3, and receives the column
+// 32 db + l32 of those 4 rows.
+__device__ __forceinline__ bf16x8 v_operand(const __bf16* sV, int s4, int db, int lane) {
+  const int grp = lane >> 4, s = lane & 15;
+  const int h = grp >> 1;
+  const __bf16* base = sV + (16 * s4 + 4 * h + (s >> 2)) * VSR + 32 * db + 16 * (grp & 1) + 4 * (s & 3);
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + 8 * VSR));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 struct DenseTiles {
   int pos, N;
@@ -163,13 +144,124 @@ struct SparseTiles {
   }
 };
 
-template <int NW, int R, bool OUT_F32, bool SPARSE>
-__global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_bf16_kernel(AttnArgs a) {
+// S^T for one 64-key tile: sacc[kb][r] holds key 32 kb + (r/4)*8 + 4h + r%4
+// of query row l32.
+__device__ __forceinline__ void qk_tile(f32x16 (&sacc)[2], const __bf16* sK, const bf16x8 (&qf)[8],
+                                        int l32, int h) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (kb * 32 + l32) * KS + 16 * s + 8 * h);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
+    }
+}
+
+// Keep a value computed at this point of the instruction stream: an empty
+// asm that reads and writes the register stops IR passes from sinking the
+// computation past the interleave points below (sched_barrier only binds
+// the machine scheduler).
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
+struct RowState {
+  float m;    // running max of the raw dot products P is taken against
+  float mc;   // m * c (0 until the first tile sets it)
+  float l;    // this lane's partial sum of the rounded P
+};
+
+// Row max / sum over both lane halves of one query row (lanes l and l^32).
+__device__ __forceinline__ float row_max_halves(float x) { return fmaxf(x, swap_halves(x)); }
+__device__ __forceinline__ float row_sum_halves(float x) { return x + swap_halves(x); }
+
+// Move the running max when some row of the wave grew past the lazy bound
+// (t is the tile's row max), rescaling O and l.
+__device__ __forceinline__ void maybe_rescale(float t, RowState& st, f32x16 (&oacc)[4], float c) {
+  const bool grow = (t - st.m) * c > kLazy;
+  if (__any(grow)) {
+    const float mnew = fmaxf(st.m, t);
+    const float alpha = fast_exp2((st.m - mnew) * c);
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    st.m = mnew;
+    st.mc = mnew * c;
+  }
+}
+
+__device__ __forceinline__ float tile_max(const f32x16 (&sacc)[2]) {
+  float t = sacc[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[kb][r]);
+  return row_max_halves(t);
+}
+
+// Elements 2i and 2i+1 of the tile: P = 2^(S c - m c), rounded to a bf16
+// pair, and its rounded sum added to ls.
+__device__ __forceinline__ void exp_pair(const f32x16 (&sacc)[2], int i, float mc, float c,
+                                         uint32_t (&pk)[2][8], float& ls) {
+  const int kb = i >> 3, r = 2 * (i & 7);
+  const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][r], c, -mc));
+  const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][r + 1], c, -mc));
+  pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+  ls = sum_bf16x2(pk[kb][r >> 1], ls);
+}
+
+__device__ __forceinline__ void exp_tile(const f32x16 (&sacc)[2], RowState& st, uint32_t (&pk)[2][8], float c) {
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) exp_pair(sacc, i, st.mc, c, pk, ls[i & 3]);
+  st.l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+}
+
+__device__ __forceinline__ bf16x8 p_operand(const uint32_t (&pk)[2][8], int s4) {
+  u32x4 t;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) t[w] = pk[s4 >> 1][4 * (s4 & 1) + w];
+  return __builtin_bit_cast(bf16x8, t);
+}
+
+__device__ __forceinline__ void pv_tile(f32x16 (&oacc)[4], const uint32_t (&pk)[2][8], const __bf16* sV,
+                                        int lane) {
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const bf16x8 pf = p_operand(pk, s4);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(sV, s4, db, lane), pf, oacc[db], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void mask_tail(f32x16 (&sacc)[2], int key0, int N, int h) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+      if (key >= N) sacc[kb][r] = -INFINITY;
+    }
+}
+
+// NBUF = 3: three rotating tile buffers and the offset two-wave pipeline
+// below (8 waves, one work-group per CU).  NBUF = 2: double buffering with
+// one tile in flight and a plain per-tile loop (4 waves; two work-groups fit
+// a CU, which is what the block-sparse launch uses).  Per query row both
+// perform the same operations on the same tiles in the same order.
+template <int NW, int NBUF, bool OUT_F32, bool SPARSE>
+__global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int BM = NW * 32 * R;
+  constexpr int BM = NW * 32;
   static_assert(!SPARSE || BM == kBlock, "block-sparse work-groups cover one 128-row mask block");
-  __shared__ __attribute__((aligned(16))) __bf16 smK[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 smV[2][D * VS];
+  __shared__ __attribute__((aligned(16))) __bf16 smK[NBUF][BN * KS];
+  __shared__ __attribute__((aligned(16))) __bf16 smV[NBUF][BN * VSR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -188,34 +280,21 @@ __global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_bf16_kernel(At
   const uint32_t qrow = (uint32_t)(a.qs[2] * 2), krow = (uint32_t)(a.ks[2] * 2),
                  vrow = (uint32_t)(a.vs[2] * 2);
 
-  const int q0 = qblk * BM + wave * 32 * R;
+  const int q0 = qblk * BM + wave * 32;
 
-  // Q as the B operand of S^T = K Q^T: lane (l32, h) holds row q0 + 32 qi + l32,
+  // Q as the B operand of S^T = K Q^T: lane (l32, h) holds row q0 + l32,
   // d = 16 s + 8 h .. +7 for step s.  Rows >= N load as zero.
-  bf16x8 qf[R][8];
+  bf16x8 qf[8];
 #pragma unroll
-  for (int qi = 0; qi < R; ++qi)
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qf[qi][s] = __builtin_bit_cast(
-          bf16x8, buf_load_b128(rq, (uint32_t)(q0 + qi * 32 + l32) * qrow + (16 * s + 8 * h) * 2));
+  for (int s = 0; s < 8; ++s)
+    qf[s] = __builtin_bit_cast(bf16x8, buf_load_b128(rq, (uint32_t)(q0 + l32) * qrow + (16 * s + 8 * h) * 2));
 
-  f32x16 oacc[R][4];
+  f32x16 oacc[4];
 #pragma unroll
-  for (int qi = 0; qi < R; ++qi)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qi][db][r] = 0.f;
-  // m_run: running max of the raw dot products (the value P is taken
-  // against), mc_run = m_run * c (0 until the first tile sets it).
-  float m_run[R], mc_run[R], l_run[R];
-#pragma unroll
-  for (int qi = 0; qi < R; ++qi) {
-    m_run[qi] = -INFINITY;
-    mc_run[qi] = 0.f;
-    l_run[qi] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  RowState st = {-INFINITY, 0.f, 0.f};
 
   typename std::conditional<SPARSE, SparseTiles, DenseTiles>::type tiles;
   if constexpr (SPARSE) {
@@ -231,168 +310,135 @@ __global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_bf16_kernel(At
   }
 
   TileLoader<NT> ld;
-  int k_cur = tiles.next();
-  if (k_cur >= 0) {
-    ld.load(rk, rv, krow, vrow, k_cur, tid);
-    ld.store(smK[0], smV[0], tid);
-  }
-  int k_nxt = tiles.next();
-  if (k_nxt >= 0) ld.load(rk, rv, krow, vrow, k_nxt, tid);
-  __syncthreads();
-
-  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK is set
-  // only for the ragged last tile, so full tiles carry no key compares.
-  auto tile_body = [&](auto mask_tag, const __bf16* sK, const __bf16* sV, int k_cur) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    f32x16 sacc[R][2];
-#pragma unroll
-    for (int qi = 0; qi < R; ++qi)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qi][kb][r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (kb * 32 + l32) * KS + 16 * s + 8 * h);
-#pragma unroll
-        for (int qi = 0; qi < R; ++qi)
-          sacc[qi][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qi][s], sacc[qi][kb], 0, 0, 0);
+  const int k0 = tiles.next();
+  if constexpr (NBUF == 3) {
+    // ---- prologue: tiles 0 and 1 into LDS, tile 2 into registers ----
+    int k1 = -1, k2 = -1;
+    if (k0 >= 0) {
+      ld.load(rk, rv, krow, vrow, k0, tid);
+      ld.store(smK[0], smV[0], tid);
+      k1 = tiles.next();
+      if (k1 >= 0) {
+        ld.load(rk, rv, krow, vrow, k1, tid);
+        ld.store(smK[1], smV[1], tid);
+        k2 = tiles.next();
+        if (k2 >= 0) ld.load(rk, rv, krow, vrow, k2, tid);
       }
-    }
-
-    if constexpr (MASK) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k_cur + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (key >= N) {
-#pragma unroll
-            for (int qi = 0; qi < R; ++qi) sacc[qi][kb][r] = -INFINITY;
-          }
-        }
-    }
-
-    // Row max of the tile; the running max moves (and O, l are rescaled)
-    // only when some row of the wave gains more than 2^kLazy, so most
-    // tiles skip the rescale of the 64 x 128 accumulator.
-    float mx[R];
-    bool grow = false;
-#pragma unroll
-    for (int qi = 0; qi < R; ++qi) {
-      float t = sacc[qi][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[qi][kb][r]);
-      t = fmaxf(t, swap_halves(t));
-      mx[qi] = t;
-      grow |= (t - m_run[qi]) * c > kLazy;
-    }
-    if (__any(grow)) {
-#pragma unroll
-      for (int qi = 0; qi < R; ++qi) {
-        const float mnew = fmaxf(m_run[qi], mx[qi]);
-        const float alpha = fast_exp2((m_run[qi] - mnew) * c);
-        l_run[qi] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qi][db][r] *= alpha;
-        m_run[qi] = mnew;
-        mc_run[qi] = mnew * c;
-      }
-    }
-
-    // P rounded to bf16 (round to nearest even) feeds the PV product, and the
-    // row sum is taken over those same rounded weights (one v_dot2 with
-    // (1, 1) per pair), so the normalised weights stay a convex combination
-    // even when a single key dominates the row.
-    uint32_t pk[R][2][8];   // P as packed bf16 pairs, [qi][kb][pair]
-#pragma unroll
-    for (int qi = 0; qi < R; ++qi) {
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(sacc[qi][kb][r], c, -mc_run[qi]));
-          const float p1 = fast_exp2(__builtin_fmaf(sacc[qi][kb][r + 1], c, -mc_run[qi]));
-          pk[qi][kb][r >> 1] = pack_bf16x2(p0, p1);
-          ls[(r >> 1) & 3] = sum_bf16x2(pk[qi][kb][r >> 1], ls[(r >> 1) & 3]);
-        }
-      l_run[qi] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    }
-
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      bf16x8 pf[R];
-#pragma unroll
-      for (int qi = 0; qi < R; ++qi) {
-        u32x4 t;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) t[w] = pk[qi][s4 >> 1][4 * (s4 & 1) + w];
-        pf[qi] = __builtin_bit_cast(bf16x8, t);
-      }
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + (db * 32 + l32) * VS + 16 * s4 + 8 * h);
-#pragma unroll
-        for (int qi = 0; qi < R; ++qi)
-          oacc[qi][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qi], oacc[qi][db], 0, 0, 0);
-      }
-    }
-  };
-
-  // Full tiles; the ragged tile (if any) holds key N - 1 and so comes last
-  // in both the dense and the block-sparse order: it runs after the loop.
-  int buf = 0;
-  while (k_cur >= 0 && k_cur + BN <= N) {
-    tile_body(std::false_type{}, smK[buf], smV[buf], k_cur);
-
-    int k_nn = -1;
-    if (k_nxt >= 0) {
-      ld.store(smK[buf ^ 1], smV[buf ^ 1], tid);
-      k_nn = tiles.next();
-      if (k_nn >= 0) ld.load(rk, rv, krow, vrow, k_nn, tid);
     }
     __syncthreads();
-    k_cur = k_nxt;
-    k_nxt = k_nn;
-    buf ^= 1;
+
+    if (k0 >= 0) {
+      f32x16 sacc[2];
+      uint32_t pk[2][8];
+      qk_tile(sacc, smK[0], qf, l32, h);
+      if (k0 + BN > N) mask_tail(sacc, k0, N, h);
+      maybe_rescale(tile_max(sacc), st, oacc, c);
+      exp_tile(sacc, st, pk, c);
+      int kn = k1, kn2 = k2;
+      int bc = 0;   // LDS buffer of the current tile; kn sits in bc+1, kn2 goes to bc+2 (mod 3)
+
+      // ---- steady state: step t = [QK^T(t+1), PV(t)] then [softmax(t+1)] ----
+      // The two waves that share a SIMD are offset by half a step: waves
+      // 0..NW/2-1 reach the barrier after the softmax, the others after the
+      // MFMA block, so while one runs its 32 MFMAs the other can run its
+      // vector work.  One barrier per step and wave orders the buffer reuse.
+      const bool late = wave >= NW / 2;
+      while (kn >= 0 && kn + BN <= N) {
+        const int bn = (bc + 1 == NBUF) ? 0 : bc + 1;
+        const int bn2 = (bn + 1 == NBUF) ? 0 : bn + 1;
+        int kn3 = -1;
+        if (kn2 >= 0) {
+          ld.store(smK[bn2], smV[bn2], tid);
+          kn3 = tiles.next();
+          if (kn3 >= 0) ld.load(rk, rv, krow, vrow, kn3, tid);
+        }
+        qk_tile(sacc, smK[bn], qf, l32, h);
+        pv_tile(oacc, pk, smV[bc], lane);
+        if (late) __syncthreads();
+        maybe_rescale(tile_max(sacc), st, oacc, c);
+        exp_tile(sacc, st, pk, c);
+        if (!late) __syncthreads();
+        kn = kn2;
+        kn2 = kn3;
+        bc = bn;
+      }
+
+      // ---- drain: PV of the current tile, then a ragged last tile if there
+      // is one (already in LDS; keys past N get -inf) ----
+      pv_tile(oacc, pk, smV[bc], lane);
+      if (kn >= 0) {
+        const int bn = (bc + 1 == NBUF) ? 0 : bc + 1;
+        qk_tile(sacc, smK[bn], qf, l32, h);
+        mask_tail(sacc, kn, N, h);
+        maybe_rescale(tile_max(sacc), st, oacc, c);
+        exp_tile(sacc, st, pk, c);
+        pv_tile(oacc, pk, smV[bn], lane);
+      }
+    }
+  } else {
+    // ---- prologue: tile 0 into LDS, tile 1 into registers ----
+    int k1 = -1;
+    if (k0 >= 0) {
+      ld.load(rk, rv, krow, vrow, k0, tid);
+      ld.store(smK[0], smV[0], tid);
+      k1 = tiles.next();
+      if (k1 >= 0) ld.load(rk, rv, krow, vrow, k1, tid);
+    }
+    __syncthreads();
+
+    f32x16 sacc[2];
+    uint32_t pk[2][8];
+    int kc = k0, kn = k1, bc = 0;
+    while (kc >= 0 && kc + BN <= N) {
+      qk_tile(sacc, smK[bc], qf, l32, h);
+      maybe_rescale(tile_max(sacc), st, oacc, c);
+      exp_tile(sacc, st, pk, c);
+      pv_tile(oacc, pk, smV[bc], lane);
+      int kn2 = -1;
+      if (kn >= 0) {
+        ld.store(smK[bc ^ 1], smV[bc ^ 1], tid);
+        kn2 = tiles.next();
+        if (kn2 >= 0) ld.load(rk, rv, krow, vrow, kn2, tid);
+      }
+      __syncthreads();
+      kc = kn;
+      kn = kn2;
+      bc ^= 1;
+    }
+    if (kc >= 0) {   // ragged last tile
+      qk_tile(sacc, smK[bc], qf, l32, h);
+      mask_tail(sacc, kc, N, h);
+      maybe_rescale(tile_max(sacc), st, oacc, c);
+      exp_tile(sacc, st, pk, c);
+      pv_tile(oacc, pk, smV[bc], lane);
+    }
   }
-  if (k_cur >= 0) tile_body(std::true_type{}, smK[buf], smV[buf], k_cur);
 
   // ---- epilogue ----
   const int64_t ob = b * a.os[0] + hd * a.os[1];
+  const float lt = row_sum_halves(st.l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int row = q0 + l32;
+  if (row < N) {
+    const int64_t orow = ob + (int64_t)row * a.os[2];
 #pragma unroll
-  for (int qi = 0; qi < R; ++qi) {
-    const float lt = l_run[qi] + swap_halves(l_run[qi]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int row = q0 + qi * 32 + l32;
-    if (row < N) {
-      const int64_t orow = ob + (int64_t)row * a.os[2];
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = db * 32 + r4 * 8 + h * 4;
-          const float v0 = oacc[qi][db][4 * r4 + 0] * inv, v1 = oacc[qi][db][4 * r4 + 1] * inv;
-          const float v2 = oacc[qi][db][4 * r4 + 2] * inv, v3 = oacc[qi][db][4 * r4 + 3] * inv;
-          if constexpr (OUT_F32) {
-            f32x4 t = {v0, v1, v2, v3};
-            *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d0) = t;
-          } else {
-            u32x2 t = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + orow + d0) = t;
-          }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + r4 * 8 + h * 4;
+        const float v0 = oacc[db][4 * r4 + 0] * inv, v1 = oacc[db][4 * r4 + 1] * inv;
+        const float v2 = oacc[db][4 * r4 + 2] * inv, v3 = oacc[db][4 * r4 + 3] * inv;
+        if constexpr (OUT_F32) {
+          f32x4 t = {v0, v1, v2, v3};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d0) = t;
+        } else {
+          u32x2 t = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + orow + d0) = t;
         }
-      if (a.lse != nullptr && h == 0)
-        a.lse[(int64_t)bh * N + row] =
-            lt > 0.f ? (m_run[qi] * c + __builtin_log2f(lt)) * 0.69314718055994530942f : -INFINITY;
-    }
+      }
+    if (a.lse != nullptr && h == 0)
+      a.lse[(int64_t)bh * N + row] =
+          lt > 0.f ? (st.mc + __builtin_log2f(lt)) * 0.69314718055994530942f : -INFINITY;
   }
 }
 
@@ -405,11 +451,11 @@ hipError_t launch_attn_bf16(const AttnArgs& args, bool out_f32, bool sparse, hip
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)nwg);
   if (sparse) {
-    if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<4, 1, true, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<4, 1, false, true>), grid, dim3(256), 0, s, a);
+    if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<4, 2, true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<4, 2, false, true>), grid, dim3(256), 0, s, a);
   } else {
-    if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<8, 1, true, false>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<8, 1, false, false>), grid, dim3(512), 0, s, a);
+    if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<8, 3, true, false>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<8, 3, false, false>), grid, dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }
