@@ -9,8 +9,8 @@
 //   order the PV operand reads them, so the attention kernel copies tiles
 //   into LDS without any shuffle.
 //
-// Attention (work-group = 4 waves x 64 query rows, key tiles of 128 = one
-// scale block), per tile with the 32x32x64 f8f6f4 MFMA:
+// Attention (work-group = 8 waves x 32 query rows, two waves per SIMD; key
+// tiles of 128 = one scale block), per tile with the 32x32x64 f8f6f4 MFMA:
 //   S^T = K8 Q8^T                    raw integer-grid dot products (fp32)
 //   t = S * (sQ sK scale log2 e)     logits in log2 units
 //   m' = max(m, rowmax t), alpha = 2^(m - m')
@@ -138,9 +138,11 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(Fp8Args a) {
 constexpr int BN8 = 128;        // keys per tile = one scale block
 constexpr int RS8 = 128 + 16;   // LDS row stride in bytes (conflict-free 16-byte reads)
 
-template <bool OUT_F32>
-__global__ __launch_bounds__(256) void attn_fp8_kernel(Fp8Args a, int nqb) {
-  constexpr int NW = 4, R = 2, BM = NW * 32 * R, NT = NW * 64;
+template <int NW, int R, bool OUT_F32>
+__global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_fp8_kernel(Fp8Args a, int nqb) {
+  constexpr int BM = NW * 32 * R, NT = NW * 64;
+  constexpr int KCH = BN8 * (D / 16) / NT;   // 16-byte chunks of each of K8 and V8t per thread
+  static_assert(KCH * NT == BN8 * (D / 16), "tile split");
   __shared__ __attribute__((aligned(16))) uint8_t smK[2][BN8 * RS8];
   __shared__ __attribute__((aligned(16))) uint8_t smV[2][D * RS8];
 
@@ -188,11 +190,11 @@ __global__ __launch_bounds__(256) void attn_fp8_kernel(Fp8Args a, int nqb) {
   }
   float sv_prev = 1.f;
 
-  // tile loader: 4 x 16 B of K8 and 4 x 16 B of V8t per thread
-  u32x4 kr[4], vr[4];
+  // tile loader: KCH x 16 B of K8 and of V8t per thread
+  u32x4 kr[KCH], vr[KCH];
   auto load_tile = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < KCH; ++i) {
       const int id = tid + i * NT, row = id >> 3, c = id & 7;
       kr[i] = buf_load_b128(rk, (uint32_t)(t * BN8 + row) * D + c * 16);
       vr[i] = buf_load_b128(rv, (uint32_t)row * np + t * BN8 + c * 16);
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(256) void attn_fp8_kernel(Fp8Args a, int nqb) {
   };
   auto store_tile = [&](int bf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < KCH; ++i) {
       const int id = tid + i * NT, row = id >> 3, c = id & 7;
       *reinterpret_cast<u32x4*>(&smK[bf][row * RS8 + c * 16]) = kr[i];
       *reinterpret_cast<u32x4*>(&smV[bf][row * RS8 + c * 16]) = vr[i];
@@ -356,11 +358,11 @@ hipError_t launch_fp8_quantize(const Fp8Args& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_fp8(const Fp8Args& a, bool out_f32, hipStream_t s) {
-  const int nqb = (a.N + 255) / 256;
+  const int nqb = (a.N + 255) / 256;   // 8 waves x 32 query rows per work-group
   const int64_t nwg = (int64_t)a.B * a.H * nqb;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (out_f32) hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, s, a, nqb);
-  else hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, s, a, nqb);
+  if (out_f32) hipLaunchKernelGGL((attn_fp8_kernel<8, 1, true>), dim3((unsigned)nwg), dim3(512), 0, s, a, nqb);
+  else hipLaunchKernelGGL((attn_fp8_kernel<8, 1, false>), dim3((unsigned)nwg), dim3(512), 0, s, a, nqb);
   return hipGetLastError();
 }
 
