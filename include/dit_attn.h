@@ -102,7 +102,8 @@ size_t dit_attn_fwd_fp8_workspace_bytes(const dit_attn_shape* shape);
  * (absmax == 0 gives s = 1 and zero codes).  QK^T runs on fp8 MFMA; the
  * online softmax keeps a running max per 128-key block; the unnormalised
  * probabilities w in [0, 1] are quantised as e4m3(448 w) for the fp8 PV
- * product; the row sum uses the unquantised w; output is bf16 (or fp32).
+ * product, and the row sum is taken over the same quantised weights (so the
+ * normalised weights sum to one); output is bf16 (or fp32).
  * The quantisation pass writes the workspace (layout above), then the
  * attention pass reads it, both on `stream`. */
 int dit_attn_fwd_fp8(const dit_attn_shape* shape,

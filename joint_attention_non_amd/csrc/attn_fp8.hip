@@ -15,7 +15,8 @@
 //   t = S * (sQ sK scale log2 e)     logits in log2 units
 //   m' = max(m, rowmax t), alpha = 2^(m - m')
 //   y = 2^(t - m' + log2 448)        = 448 w with w in [0, 1]
-//   l = alpha l + sum y              (row sum of the unquantised weights)
+//   l = alpha l + sum e4m3(y)        (row sum of the quantised weights, on
+//                                     the MFMA with an all-ones operand)
 //   A = A * alpha * sV_prev / sV + V8^T e4m3(y)^T
 // and at the end O = A * sV_last / l, lse = ln2 (m + log2(l / 448)).
 #include "device_common.h"
@@ -182,12 +183,16 @@ __global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_fp8_kernel(Fp8
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qi][db][r] = 0.f;
-  float m_run[R], l_run[R];
+  float m_run[R];
+  f32x16 lacc[R];   // row sums of the quantised weights (448 units), element 0 used
 #pragma unroll
   for (int qi = 0; qi < R; ++qi) {
     m_run[qi] = -INFINITY;
-    l_run[qi] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lacc[qi][r] = 0.f;
   }
+  const i32x8 kOnes = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                       0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
   float sv_prev = 1.f;
 
   // tile loader: KCH x 16 B of K8 and of V8t per thread
@@ -270,7 +275,6 @@ __global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_fp8_kernel(Fp8
       const float mnew = fmaxf(m_run[qi], mx * f);
       const float alpha = fast_exp2(m_run[qi] - mnew);
       const float moff = mnew - a.p_off;
-      float ls = 0.f;
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -280,11 +284,11 @@ __global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_fp8_kernel(Fp8
           for (int e = 0; e < 4; ++e) {
             const int slot = 4 * w + e, kb = 2 * s + (slot >> 4), r = slot & 15;
             y[e] = fast_exp2(__builtin_fmaf(sacc[qi][kb][r], f, -moff));
-            ls += y[e];
           }
           p8[qi][s][w] = cvt4_e4m3(y[0], y[1], y[2], y[3]);
         }
-      l_run[qi] = l_run[qi] * alpha + ls;
+      // Only element 0 of the row-sum accumulator is read (see below).
+      lacc[qi][0] *= alpha;
       m_run[qi] = mnew;
       const float g = alpha * vratio;
 #pragma unroll
@@ -306,6 +310,11 @@ __global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_fp8_kernel(Fp8
           const i32x8 pf = {(int)p8[qi][s][0], (int)p8[qi][s][1], (int)p8[qi][s][2], (int)p8[qi][s][3],
                             (int)p8[qi][s][4], (int)p8[qi][s][5], (int)p8[qi][s][6], (int)p8[qi][s][7]};
           oacc[qi][db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, oacc[qi][db], 0, 0, 0, 0, 0, 0);
+          // Row sum of the quantised weights on the matrix core: an all-ones
+          // A operand makes every row of the 32x32 result the column sum of
+          // P8, so each lane gets its query row's sum in every register.
+          if (db == 0)
+            lacc[qi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kOnes, pf, lacc[qi], 0, 0, 0, 0, 0, 0);
         }
       }
 
@@ -320,7 +329,7 @@ __global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_fp8_kernel(Fp8
   const int64_t ob = b * a.os[0] + hd * a.os[1];
 #pragma unroll
   for (int qi = 0; qi < R; ++qi) {
-    const float lt = l_run[qi] + swap_halves(l_run[qi]);
+    const float lt = lacc[qi][0];
     const float inv = lt > 0.f ? sv_prev / lt : 0.f;
     const int row = q0 + qi * 32 + l32;
     if (row < N) {

@@ -171,7 +171,10 @@ int prepare_fp8(const dit_attn_shape* sh, const void* q, const void* k, const vo
   f.sk = reinterpret_cast<float*>(base + L.sk);
   f.sv = reinterpret_cast<float*>(base + L.sv);
   f.c = (float)((double)sh->softmax_scale * 1.4426950408889634);
-  float off = (float)std::log2(448.0);
+  // 448 w = 2^(x + p_off) with p_off just below log2(448): the margin of
+  // 2^-14 covers the rounding of the running max, so the product never
+  // exceeds 448 before it is converted to e4m3 (w <= 1).
+  float off = (float)(std::log2(448.0) - 1.0 / 16384.0);
   while (std::exp2((double)off) > 448.0) off = std::nextafter(off, 0.f);
   f.p_off = off;
   return DIT_ATTN_OK;

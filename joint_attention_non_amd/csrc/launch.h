@@ -40,7 +40,7 @@ struct Fp8Args {
   float* sk;
   float* sv;
   float c;              // softmax_scale * log2(e)
-  float p_off;          // log2(448) rounded down: w * 448 = exp2(x + p_off)
+  float p_off;          // just below log2(448): w * 448 = exp2(x + p_off) <= 448
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool out_f32, bool sparse, hipStream_t s);

@@ -216,7 +216,8 @@ void oracle_fp8_quantize(int64_t BH, int64_t N, int64_t D, int64_t block,
  *   m_kb  = max(m_{kb-1}, max_{j in kb} t_j)                 (running max)
  *   w_j   = exp(t_j - m_kb)                                  (in [0, 1])
  *   P8_j  = e4m3(448 * w_j)          if quantize_p, else 448 * w_j
- *   l     = exp(m_{kb-1} - m_kb) * l + sum_j w_j             (row sum from w)
+ *   l     = exp(m_{kb-1} - m_kb) * l + sum_j P8_j / 448      (the same weights
+ *                                                             that multiply V)
  *   acc_d = exp(m_{kb-1} - m_kb) * acc_d + sum_j (P8_j / 448) * sv[kb] * dec(v8_jd)
  *   o_d   = acc_d / l,   lse = m_last + ln l
  *
@@ -274,9 +275,9 @@ int oracle_attn_fp8_recipe(int64_t BH, int64_t N, int64_t D, int64_t block,
                     const double svk = (double)sv[bh * nb + kb];
                     for (int64_t j = j0; j < j1; ++j) {
                         const double w = exp(t[j - j0] - mnew);
-                        l += w;
                         const float y = (float)w * 448.0f;
                         const double p = quantize_p ? dec[oracle_e4m3_encode((double)y)] : 448.0 * w;
+                        l += p / 448.0;
                         const double c = p / 448.0 * svk;
                         for (int64_t d = 0; d < D; ++d) acc[d] += c * dec[v8[(bh * N + j) * D + d]];
                     }

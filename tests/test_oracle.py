@@ -349,7 +349,7 @@ def test_fp8_recipe_one_hot_key_returns_dequantised_value_row():
 
 def test_fp8_recipe_single_block_closed_form():
     """N <= 128: one key block, so the running max is the row max and the
-    recipe is O = sum_j dec(e4m3(448 w_j)) / 448 * V_j / sum_j w_j."""
+    recipe is O = sum_j p_j V_j / sum_j p_j with p_j = dec(e4m3(448 w_j)) / 448."""
     (q, k, v), (q8, k8, v8, sq, sk, sv) = _quantized_inputs(96, 17)
     scale = 1.0 / math.sqrt(128)
     o, _ = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale)
@@ -358,7 +358,7 @@ def test_fp8_recipe_single_block_closed_form():
     w = np.exp(t - t.max(axis=1, keepdims=True))
     p8 = torch.from_numpy((w.astype(np.float32) * np.float32(448.0))).to(torch.float8_e4m3fn)
     p = p8.to(torch.float64).numpy() / 448.0
-    ref = (p @ vd) / w.sum(axis=1, keepdims=True)
+    ref = (p @ vd) / p.sum(axis=1, keepdims=True)
     assert np.max(np.abs(o[0, 0] - ref)) <= 1e-12
 
 
