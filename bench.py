@@ -77,15 +77,23 @@ def _traffic(kernel_key: str, sha: str):
     return rec.get("bytes_per_launch")
 
 
-def _cpu_baseline(w, q, k, v, budget_s=15.0):
+def _cpu_baseline(w, q, k, v, budget_s=18.0):
+    """The fp64 oracle on the host cores, on a bounded sample of query rows of
+    the headline workload (every key of the row's (b, h) slice): a probe of a
+    few hundred rows sizes the sample to about budget_s seconds."""
     import oracle
     from workloads import sample_rows
     qd, kd, vd = (t.double().numpy() for t in (q, k, v))
-    probe = sample_rows(w.batch, w.heads, w.seqlen, 64, seed=1)
-    t0 = time.perf_counter()
-    oracle.attn(qd, kd, vd, w.scale, rows=probe)
-    dt = time.perf_counter() - t0
-    n = int(max(64, min(200000, len(probe) * budget_s / max(dt, 1e-6))))
+    n_probe, dt = 512, 0.0
+    while True:
+        probe = sample_rows(w.batch, w.heads, w.seqlen, n_probe, seed=1)
+        t0 = time.perf_counter()
+        oracle.attn(qd, kd, vd, w.scale, rows=probe)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 or n_probe >= 65536:
+            break
+        n_probe *= 4
+    n = int(max(64, min(400000, len(probe) * budget_s / max(dt, 1e-6))))
     rows = sample_rows(w.batch, w.heads, w.seqlen, n, seed=2)
     t0 = time.perf_counter()
     oracle.attn(qd, kd, vd, w.scale, rows=rows)
@@ -108,6 +116,9 @@ def main():
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one device-to-device copy of MIB MiB (a kernel of "
                          "known traffic, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--i2i", action="store_true",
+                    help="also time the dense kernel on the image-to-image joint sequence "
+                         "(512 text + 16384 target + 16384 reference tokens, B=2)")
     ap.add_argument("--img1024", action="store_true",
                     help="also time the dense kernel at the 1024^2 shape (same kernel name as "
                          "the headline, so keep it out of profiled runs)")
@@ -145,7 +156,7 @@ def main():
     traffic = _traffic("attn_bf16_img2048", sha)
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "attn_bf16_kernel<8,false,false>",
+                "traffic": traffic, "kernel": "attn_bf16_kernel<8,3,false,false>",
                 "flops_per_launch": flops}
     log(f"[bench] {w.name}: {ms:.3f} ms  {tflops:.1f} TFLOP/s  {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
     del o
@@ -202,12 +213,16 @@ def main():
         log(f"[bench] {wsp.name}: {legs[wsp.name]}")
         del qs, ks, vs, md, os_
 
-    if args.img1024:
-        w1 = WORKLOADS["img1024"]
+    for flag, wname in ((args.i2i, "i2i2048"), (args.img1024, "img1024")):
+        if not flag:
+            continue
+        w1 = WORKLOADS[wname]
+        log(f"[bench] leg {w1.name}")
         q1, k1, v1, _ = make_workload_inputs(w1, seed=0)
         q1, k1, v1 = (t.to(dev) for t in (q1, k1, v1))
         o1 = torch.empty_like(q1)
-        ms_1 = _time_launches(lambda: dit.attn_fwd(q1, k1, v1, out=o1), max(args.steps, 50),
+        ms_1 = _time_launches(lambda: dit.attn_fwd(q1, k1, v1, out=o1),
+                              max(args.steps, 50) if w1.seqlen < 8192 else args.steps,
                               args.warmup, torch)
         f1 = _flops_dense(w1.batch, w1.heads, w1.seqlen, w1.head_dim)
         legs[w1.name] = {"ms": round(ms_1, 4), "achieved": round(f1 / (ms_1 * 1e-3) / 1e12, 2),

@@ -138,3 +138,8 @@ def test_img1024_sampled_parity():
 
 def test_img2048_cfg_pair_sampled_parity():
     _sampled_parity("img2048", 384)
+
+
+def test_i2i2048_sampled_parity():
+    """Image-to-image joint sequence: text + target + reference latents."""
+    _sampled_parity("i2i2048", 256)

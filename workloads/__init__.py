@@ -13,6 +13,9 @@ Workloads (all non-causal, head_dim 128, softmax scale 1/sqrt(128)):
 * ``img2048_fp8``    B=1 H=24 N=16896, e4m3 recipe
 * ``img2048_sparse`` B=1 H=24 N=16896, 128x128 block mask, density 0.25 with
   the diagonal and every text-token block forced on
+* ``i2i2048``   B=2 H=24 N=512+16384+16384=33280: image-to-image at 2048^2,
+  where the joint sequence also carries the reference image's latents (taken
+  at the target resolution), 1% of key rows x8
 
 The token order is text first, then image latents: joint attention in the
 FLUX-family DiT concatenates the separately embedded text, target-image and
@@ -91,6 +94,8 @@ WORKLOADS = {
     "img2048_fp8": Workload("img2048_fp8", 1, 24, 512, 16384, variant="fp8"),
     "img2048_sparse": Workload("img2048_sparse", 1, 24, 512, 16384, variant="sparse",
                                mask_density=0.25),
+    # text + target latents + reference-image latents
+    "i2i2048": Workload("i2i2048", 2, 24, 512, 16384 + 16384, peaked_key_frac=0.01),
 }
 
 
