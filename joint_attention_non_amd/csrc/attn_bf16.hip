@@ -55,28 +55,42 @@ constexpr float kLazy = 8.f;
 // round-robin over the work-group, K first.
 template <int NT>
 struct TileLoader {
-  static constexpr int CHUNKS = 2 * BN * (D / 8);
-  static constexpr int CH = CHUNKS / NT;
-  static_assert(CH * NT == CHUNKS && (BN * (D / 8)) % NT == 0, "tile split");
+  static constexpr int KCH = BN * (D / 8) / NT;   // K chunks per thread; V has as many
+  static constexpr int CH = 2 * KCH;
+  static_assert(KCH * NT == BN * (D / 8), "tile split");
   u32x4 r[CH];
 
+  // Chunk i of this thread: K for i < KCH, else V (compile-time per i, so
+  // every load takes a uniform buffer resource).
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                        uint32_t krow, uint32_t vrow, int key0, int tid) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int id = tid + i * NT;
-      const bool isk = id < BN * (D / 8);            // compile-time per i
-      const int cid = isk ? id : id - BN * (D / 8), key = cid >> 4, c = cid & 15;
+      const bool isk = i < KCH;
+      const int cid = tid + (isk ? i : i - KCH) * NT, key = cid >> 4, c = cid & 15;
       r[i] = buf_load_b128(isk ? rk : rv, (uint32_t)(key0 + key) * (isk ? krow : vrow) + c * 16);
     }
+  }
+
+  template <int I>
+  __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                           uint32_t krow, uint32_t vrow, int key0, int tid) {
+    constexpr bool isk = I < KCH;
+    const int cid = tid + (isk ? I : I - KCH) * NT, key = cid >> 4, c = cid & 15;
+    r[I] = buf_load_b128(isk ? rk : rv, (uint32_t)(key0 + key) * (isk ? krow : vrow) + c * 16);
+  }
+  template <int I>
+  __device__ __forceinline__ void store_one(__bf16* sk, __bf16* sv, int tid) const {
+    constexpr bool isk = I < KCH;
+    const int cid = tid + (isk ? I : I - KCH) * NT, key = cid >> 4, c = cid & 15;
+    *reinterpret_cast<u32x4*>((isk ? sk + key * KS : sv + key * VSR) + c * 8) = r[I];
   }
 
   __device__ __forceinline__ void store(__bf16* sk, __bf16* sv, int tid) const {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int id = tid + i * NT;
-      const bool isk = id < BN * (D / 8);
-      const int cid = isk ? id : id - BN * (D / 8), key = cid >> 4, c = cid & 15;
+      const bool isk = i < KCH;
+      const int cid = tid + (isk ? i : i - KCH) * NT, key = cid >> 4, c = cid & 15;
       *reinterpret_cast<u32x4*>((isk ? sk + key * KS : sv + key * VSR) + c * 8) = r[i];
     }
   }
@@ -195,13 +209,17 @@ __device__ __forceinline__ void maybe_rescale(float t, RowState& st, f32x16 (&oa
   }
 }
 
+// Four independent max chains (folded into v_max3 by the compiler), then
+// the lane-half exchange.
 __device__ __forceinline__ float tile_max(const f32x16 (&sacc)[2]) {
-  float t = sacc[0][0];
+  float t[4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int j = 0; j < 4; ++j) {
+    t[j] = sacc[j >> 1][8 * (j & 1)];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[kb][r]);
-  return row_max_halves(t);
+    for (int r = 1; r < 8; ++r) t[j] = fmaxf(t[j], sacc[j >> 1][8 * (j & 1) + r]);
+  }
+  return max_halves(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
 }
 
 // Elements 2i and 2i+1 of the tile: P = 2^(S c - m c), rounded to a bf16
@@ -215,10 +233,20 @@ __device__ __forceinline__ void exp_pair(const f32x16 (&sacc)[2], int i, float m
   ls = sum_bf16x2(pk[kb][r >> 1], ls);
 }
 
+// The 32 elements go through each stage together (exponent FMAs, then
+// exponentials, then packing and row sums), so that dependent instructions
+// sit far apart and one wave can keep the vector ALU busy on its own.
 __device__ __forceinline__ void exp_tile(const f32x16 (&sacc)[2], RowState& st, uint32_t (&pk)[2][8], float c) {
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(sacc[i >> 4][i & 15], c, -st.mc);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = fast_exp2(x[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pk[i >> 3][i & 7] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) exp_pair(sacc, i, st.mc, c, pk, ls[i & 3]);
+  for (int i = 0; i < 16; ++i) ls[i & 3] = sum_bf16x2(pk[i >> 3][i & 7], ls[i & 3]);
   st.l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 }
 
@@ -238,6 +266,95 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[4], const uint32_t (&pk)[
     for (int db = 0; db < 4; ++db)
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(sV, s4, db, lane), pf, oacc[db], 0, 0, 0);
   }
+}
+
+// One MFMA phase of the pipeline: S^T of the next tile (16 MFMAs, A = K
+// rows from sK) followed by O^T += V^T P^T of the current tile (16 MFMAs,
+// A = V^T from sV).  The 32 A operands are read from LDS as one stream kept
+// kPrefetch MFMAs ahead of their use, and the scheduler is told to keep that
+// interleave, so the LDS latency is covered by the matrix core's own work.
+// Riding on the PV half: the four 16-byte chunks of the staged tile are
+// stored to LDS (buffers sKs / sVs) and each register is refilled at once
+// with the global load of the tile after it (key offset kload).
+constexpr int kPrefetch = 4;
+
+template <int I>
+__device__ __forceinline__ bf16x8 step_operand(const __bf16* sK, const __bf16* sV, int l32, int h, int lane) {
+  if constexpr (I < 16) {
+    constexpr int s = I >> 1, kb = I & 1;
+    return *reinterpret_cast<const bf16x8*>(sK + (kb * 32 + l32) * KS + 16 * s + 8 * h);
+  } else {
+    constexpr int j = I - 16, s4 = j >> 2, db = j & 3;
+    return v_operand(sV, s4, db, lane);
+  }
+}
+
+template <int NT>
+struct StepLoads {
+  TileLoader<NT>& ld;
+  __bf16* sk;
+  __bf16* sv;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t krow, vrow;
+  int kload, tid;
+};
+
+template <int I, int NT>
+__device__ __forceinline__ void step_body(f32x16 (&sacc)[2], f32x16 (&oacc)[4], const bf16x8 (&qf)[8],
+                                          const uint32_t (&pk)[2][8], const __bf16* sK, const __bf16* sV,
+                                          int l32, int h, int lane, bf16x8 (&fr)[kPrefetch + 1],
+                                          const StepLoads<NT>& sl) {
+  if constexpr (I < 32) {
+    if constexpr (I + kPrefetch < 32)
+      fr[(I + kPrefetch) % (kPrefetch + 1)] = step_operand<I + kPrefetch>(sK, sV, l32, h, lane);
+    if constexpr (I < 16) {
+      constexpr int s = I >> 1, kb = I & 1;
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[I % (kPrefetch + 1)], qf[s], sacc[kb], 0, 0, 0);
+    } else {
+      constexpr int j = I - 16, s4 = j >> 2, db = j & 3;
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[I % (kPrefetch + 1)], p_operand(pk, s4),
+                                                         oacc[db], 0, 0, 0);
+      if constexpr ((j & 3) == 0) {
+        sl.ld.template store_one<j / 4>(sl.sk, sl.sv, sl.tid);
+        sl.ld.template load_one<j / 4>(sl.rk, sl.rv, sl.krow, sl.vrow, sl.kload, sl.tid);
+      }
+    }
+    step_body<I + 1, NT>(sacc, oacc, qf, pk, sK, sV, l32, h, lane, fr, sl);
+  }
+}
+
+template <int I>
+__device__ __forceinline__ void step_schedule() {
+  if constexpr (I < 32) {
+    if constexpr (I + kPrefetch < 32)
+      __builtin_amdgcn_sched_group_barrier(0x100, I + kPrefetch < 16 ? 1 : 2, 0);   // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             // one MFMA
+    if constexpr (I >= 16 && ((I - 16) & 3) == 0) {
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                           // LDS store
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                           // global load
+    }
+    step_schedule<I + 1>();
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void mfma_step(f32x16 (&sacc)[2], f32x16 (&oacc)[4], const bf16x8 (&qf)[8],
+                                          const uint32_t (&pk)[2][8], const __bf16* sK, const __bf16* sV,
+                                          int l32, int h, int lane, const StepLoads<NT>& sl) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+  bf16x8 fr[kPrefetch + 1];
+  fr[0] = step_operand<0>(sK, sV, l32, h, lane);
+  fr[1] = step_operand<1>(sK, sV, l32, h, lane);
+  fr[2] = step_operand<2>(sK, sV, l32, h, lane);
+  fr[3] = step_operand<3>(sK, sV, l32, h, lane);
+  static_assert(kPrefetch == 4, "prologue reads");
+  static_assert(TileLoader<NT>::CH == 4, "one staged chunk per PV k-step");
+  step_body<0, NT>(sacc, oacc, qf, pk, sK, sV, l32, h, lane, fr, sl);
+  __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);
+  step_schedule<0>();
 }
 
 __device__ __forceinline__ void mask_tail(f32x16 (&sacc)[2], int key0, int N, int h) {
@@ -322,8 +439,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
         ld.load(rk, rv, krow, vrow, k1, tid);
         ld.store(smK[1], smV[1], tid);
         k2 = tiles.next();
-        if (k2 >= 0) ld.load(rk, rv, krow, vrow, k2, tid);
       }
+      ld.load(rk, rv, krow, vrow, k2 >= 0 ? k2 : N, tid);
     }
     __syncthreads();
 
@@ -346,14 +463,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       while (kn >= 0 && kn + BN <= N) {
         const int bn = (bc + 1 == NBUF) ? 0 : bc + 1;
         const int bn2 = (bn + 1 == NBUF) ? 0 : bn + 1;
-        int kn3 = -1;
-        if (kn2 >= 0) {
-          ld.store(smK[bn2], smV[bn2], tid);
-          kn3 = tiles.next();
-          if (kn3 >= 0) ld.load(rk, rv, krow, vrow, kn3, tid);
-        }
-        qk_tile(sacc, smK[bn], qf, l32, h);
-        pv_tile(oacc, pk, smV[bc], lane);
+        // The staged tile goes to buffer bn2 even past the last tile (that
+        // buffer is free; nothing reads it), and loads past the end fetch
+        // key offset N, which the buffer bounds turn into zeros.
+        const int kn3 = tiles.next();
+        const StepLoads<NT> sl = {ld, smK[bn2], smV[bn2], rk, rv, krow, vrow, kn3 >= 0 ? kn3 : N, tid};
+        mfma_step<NT>(sacc, oacc, qf, pk, smK[bn], smV[bc], l32, h, lane, sl);
         if (late) __syncthreads();
         maybe_rescale(tile_max(sacc), st, oacc, c);
         exp_tile(sacc, st, pk, c);

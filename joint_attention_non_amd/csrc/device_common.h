@@ -36,6 +36,16 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max(x[l], x[l ^ 32]) in every lane l, with one v_permlane32_swap: the
+// swap of x with itself leaves x[l ^ 32] in the first result for the upper
+// half of the lanes and in the second result for the lower half.
+__device__ __forceinline__ float max_halves(float x) {
+  const uint32_t xb = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+  const uint32_t other = (threadIdx.x & 32) ? r[0] : r[1];
+  return fmaxf(x, __builtin_bit_cast(float, other));
+}
+
 // Work-group id -> logical tile id such that consecutive logical ids run on
 // the same XCD.  Work-groups are dispatched round-robin over the XCDs, so
 // physical id b lands on XCD b % 8; logical ids [x*per, (x+1)*per) are given

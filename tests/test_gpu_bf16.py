@@ -89,13 +89,21 @@ def test_bitwise_determinism():
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
 
-def test_one_hot_key_returns_value_row_bitwise():
+# (query row, dominant key) pairs for N = 300 (tiles of 64 keys, the last one
+# ragged): the key sits in either half of the 32-key accumulator blocks
+# (key % 8 < 4 or >= 4), in either block of its tile, in the first, a middle
+# and the ragged last tile, and the rows cover several waves.
+ONE_HOT_CASES = [(17, 250), (3, 68), (40, 36), (63, 299), (100, 270), (299, 7), (150, 131), (255, 190)]
+
+
+@pytest.mark.parametrize("i,j", ONE_HOT_CASES)
+def test_one_hot_key_returns_value_row_bitwise(i, j):
     """A dominant key: P = 2^0 = 1 for it, every other weight underflows to
-    0, l = 1, so O is that V row exactly."""
-    _say("case: one-hot key")
+    0, l = 1, so O is that V row exactly -- which also needs the running max
+    to be the max over every key of the row, whichever lanes hold it."""
+    _say(f"case: one-hot key i={i} j={j}")
     N = 300
     q, k, v = make_qkv(1, 1, N, 128, seed=24)
-    i, j = 17, 250
     k[0, 0, j] = (40.0 * q[0, 0, i].float()).to(torch.bfloat16)
     o = dit.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV))
     torch.cuda.synchronize()
