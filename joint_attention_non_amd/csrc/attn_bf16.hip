@@ -10,11 +10,13 @@
 //                    transposed product each lane holds 16 keys of one query
 //                    row, so the row max and row sum are in-register
 //                    reductions plus one exchange with lane l^32.
-//   online softmax   P = 2^(S c - m c) with c = scale * log2(e) and m the
-//                    running row max.  m is only moved when a row's max
-//                    grows by more than 2^8 in P units: then
-//                    alpha = 2^((m - m') c), O *= alpha, l *= alpha.  The
-//                    factor cancels in O / l, so the result is unchanged.
+//   online softmax   P = 2^(S c - m c) with c = scale * log2(e) and m a
+//                    running reference: the row max of the first tile.  Later
+//                    tiles take their exponentials against it directly; only
+//                    when a lane's weights would pass 2^64 (a row max that
+//                    grew by more than 64 bits) is m moved to the new max,
+//                    O and l rescaled and the tile redone.  The factor
+//                    cancels in O / l, so the result is unchanged.
 //   O^T += V^T P^T   A = V^T, read from the row-major V tile with the gfx950
 //                    transposing LDS read (ds_read_b64_tr_b16: 16 lanes
 //                    fetch a 4-key x 16-d block and each lane receives one d
@@ -24,10 +26,10 @@
 //                    transposing read fetches to match the order in which
 //                    the accumulator hands P out.  l accumulates the same
 //                    rounded P (v_dot2 with (1, 1)).
-// Software pipeline: step t issues the QK^T MFMAs of tile t+1 interleaved
-// with the softmax VALU work of tile t, then the PV MFMAs of tile t
-// interleaved with the LDS stores of tile t+2 and the global loads of tile
-// t+3, so the matrix cores and the vector ALUs work at the same time.
+// Software pipeline: step t issues the QK^T MFMAs of tile t+1 and the PV
+// MFMAs of tile t as one stream with their LDS operands read four MFMAs
+// ahead; the LDS stores of tile t+2 and the global loads of tile t+3 ride
+// on the PV MFMAs; then one barrier, then the softmax of tile t+1.
 // Epilogue: O = O^T / l, stored bf16 (round to nearest even) or fp32, and
 // optionally lse = ln2 * (m c + log2 l).
 //
@@ -46,8 +48,8 @@ constexpr int BN = 64;        // keys per LDS tile
 constexpr int KS = D + 8;     // K tile row stride in bf16 (272 B: conflict-free b128 reads)
 constexpr int VSR = D + 32;   // V tile row stride in bf16 (320 B: 4 consecutive rows of a
                               // transposing read land in disjoint bank quarters)
-// Lazy rescaling: P = 2^(S c - m c) may reach 2^kLazy before the running max
-// m is moved, so O and l are rescaled only on large jumps of the row max.
+// When the reference max is recomputed (first tile, or a redo after a huge
+// jump), it only moves if some row of the wave grew by more than 2^kLazy.
 constexpr float kLazy = 8.f;
 
 // Global -> register -> LDS staging of one tile: K and V both row-major
@@ -233,13 +235,14 @@ __device__ __forceinline__ void exp_pair(const f32x16 (&sacc)[2], int i, float m
   ls = sum_bf16x2(pk[kb][r >> 1], ls);
 }
 
-// The 32 elements go through each stage together (exponent FMAs, then
-// exponentials, then packing and row sums), so that dependent instructions
-// sit far apart and one wave can keep the vector ALU busy on its own.
-__device__ __forceinline__ void exp_tile(const f32x16 (&sacc)[2], RowState& st, uint32_t (&pk)[2][8], float c) {
+// P = 2^(S c - mc) for the 32 elements, rounded to bf16 pairs in pk; returns
+// this lane's sum of the rounded P.  The elements go through each stage
+// together (exponent FMAs, exponentials, packing, sums), so dependent
+// instructions sit far apart and one wave can keep the vector ALU busy.
+__device__ __forceinline__ float exp_tile_sum(const f32x16 (&sacc)[2], float mc, uint32_t (&pk)[2][8], float c) {
   float x[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(sacc[i >> 4][i & 15], c, -st.mc);
+  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(sacc[i >> 4][i & 15], c, -mc);
 #pragma unroll
   for (int i = 0; i < 32; ++i) x[i] = fast_exp2(x[i]);
 #pragma unroll
@@ -247,7 +250,33 @@ __device__ __forceinline__ void exp_tile(const f32x16 (&sacc)[2], RowState& st, 
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 16; ++i) ls[i & 3] = sum_bf16x2(pk[i >> 3][i & 7], ls[i & 3]);
-  st.l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+}
+
+// First tile of a row block: move the running max to the tile's max, then
+// take the exponentials against it.
+__device__ __forceinline__ void softmax_first(const f32x16 (&sacc)[2], RowState& st, f32x16 (&oacc)[4],
+                                              uint32_t (&pk)[2][8], float c) {
+  maybe_rescale(tile_max(sacc), st, oacc, c);
+  st.l += exp_tile_sum(sacc, st.mc, pk, c);
+}
+
+// Later tiles: take the exponentials against the current reference
+// straight away.  Weights far above 1 are harmless in floating point (the
+// row sum and O keep their relative precision), so the tile is kept unless a
+// lane's weights sum past 2^64 or overflow; only then is the reference moved
+// to the tile's max (O and l rescaled) and the tile redone.  This keeps the
+// per-tile row max out of the common path.
+// `first` (wave-uniform) forces the max pass, for the first tile of a row.
+constexpr float kCheck = 0x1p64f;   // 2^64
+__device__ __forceinline__ void softmax_next(const f32x16 (&sacc)[2], RowState& st, f32x16 (&oacc)[4],
+                                             uint32_t (&pk)[2][8], float c, bool first = false) {
+  float ls = exp_tile_sum(sacc, st.mc, pk, c);
+  if (first || __any(!(ls <= kCheck))) {
+    maybe_rescale(tile_max(sacc), st, oacc, c);
+    ls = exp_tile_sum(sacc, st.mc, pk, c);
+  }
+  st.l += ls;
 }
 
 __device__ __forceinline__ bf16x8 p_operand(const uint32_t (&pk)[2][8], int s4) {
@@ -449,17 +478,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       uint32_t pk[2][8];
       qk_tile(sacc, smK[0], qf, l32, h);
       if (k0 + BN > N) mask_tail(sacc, k0, N, h);
-      maybe_rescale(tile_max(sacc), st, oacc, c);
-      exp_tile(sacc, st, pk, c);
+      softmax_first(sacc, st, oacc, pk, c);
       int kn = k1, kn2 = k2;
       int bc = 0;   // LDS buffer of the current tile; kn sits in bc+1, kn2 goes to bc+2 (mod 3)
 
-      // ---- steady state: step t = [QK^T(t+1), PV(t)] then [softmax(t+1)] ----
-      // The two waves that share a SIMD are offset by half a step: waves
-      // 0..NW/2-1 reach the barrier after the softmax, the others after the
-      // MFMA block, so while one runs its 32 MFMAs the other can run its
-      // vector work.  One barrier per step and wave orders the buffer reuse.
-      const bool late = wave >= NW / 2;
+      // ---- steady state: step t = [QK^T(t+1), PV(t)], barrier, [softmax(t+1)] ----
+      // The barrier right after the MFMA block publishes tile t+2 (stored
+      // during the PV MFMAs) and frees tile t's buffer; the softmax needs no
+      // LDS, so it runs after it.
       while (kn >= 0 && kn + BN <= N) {
         const int bn = (bc + 1 == NBUF) ? 0 : bc + 1;
         const int bn2 = (bn + 1 == NBUF) ? 0 : bn + 1;
@@ -469,10 +495,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
         const int kn3 = tiles.next();
         const StepLoads<NT> sl = {ld, smK[bn2], smV[bn2], rk, rv, krow, vrow, kn3 >= 0 ? kn3 : N, tid};
         mfma_step<NT>(sacc, oacc, qf, pk, smK[bn], smV[bc], l32, h, lane, sl);
-        if (late) __syncthreads();
-        maybe_rescale(tile_max(sacc), st, oacc, c);
-        exp_tile(sacc, st, pk, c);
-        if (!late) __syncthreads();
+        __syncthreads();
+        softmax_next(sacc, st, oacc, pk, c);
         kn = kn2;
         kn2 = kn3;
         bc = bn;
@@ -485,8 +509,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
         const int bn = (bc + 1 == NBUF) ? 0 : bc + 1;
         qk_tile(sacc, smK[bn], qf, l32, h);
         mask_tail(sacc, kn, N, h);
-        maybe_rescale(tile_max(sacc), st, oacc, c);
-        exp_tile(sacc, st, pk, c);
+        softmax_next(sacc, st, oacc, pk, c);
         pv_tile(oacc, pk, smV[bn], lane);
       }
     }
@@ -504,10 +527,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     f32x16 sacc[2];
     uint32_t pk[2][8];
     int kc = k0, kn = k1, bc = 0;
+    bool first = true;   // wave-uniform
     while (kc >= 0 && kc + BN <= N) {
       qk_tile(sacc, smK[bc], qf, l32, h);
-      maybe_rescale(tile_max(sacc), st, oacc, c);
-      exp_tile(sacc, st, pk, c);
+      softmax_next(sacc, st, oacc, pk, c, first);
+      first = false;
       pv_tile(oacc, pk, smV[bc], lane);
       int kn2 = -1;
       if (kn >= 0) {
@@ -523,8 +547,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     if (kc >= 0) {   // ragged last tile
       qk_tile(sacc, smK[bc], qf, l32, h);
       mask_tail(sacc, kc, N, h);
-      maybe_rescale(tile_max(sacc), st, oacc, c);
-      exp_tile(sacc, st, pk, c);
+      softmax_next(sacc, st, oacc, pk, c, first);
       pv_tile(oacc, pk, smV[bc], lane);
     }
   }
