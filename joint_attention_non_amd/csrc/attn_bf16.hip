@@ -328,13 +328,16 @@ struct StepLoads {
   int kload, tid;
 };
 
-template <int I, int NT>
+// MFMAs [FIRST, LAST) of a step (0-15: QK^T, 16-31: PV).  With LOADS, the
+// CH staged chunks are stored to LDS and each register refilled from HBM,
+// spread evenly over the PV MFMAs.
+template <int I, int FIRST, int LAST, bool LOADS, int NT>
 __device__ __forceinline__ void step_body(f32x16 (&sacc)[2], f32x16 (&oacc)[4], const bf16x8 (&qf)[8],
                                           const uint32_t (&pk)[2][8], const __bf16* sK, const __bf16* sV,
                                           int l32, int h, int lane, bf16x8 (&fr)[kPrefetch + 1],
                                           const StepLoads<NT>& sl) {
-  if constexpr (I < 32) {
-    if constexpr (I + kPrefetch < 32)
+  if constexpr (I < LAST) {
+    if constexpr (I + kPrefetch < LAST)
       fr[(I + kPrefetch) % (kPrefetch + 1)] = step_operand<I + kPrefetch>(sK, sV, l32, h, lane);
     if constexpr (I < 16) {
       constexpr int s = I >> 1, kb = I & 1;
@@ -343,47 +346,61 @@ __device__ __forceinline__ void step_body(f32x16 (&sacc)[2], f32x16 (&oacc)[4], 
       constexpr int j = I - 16, s4 = j >> 2, db = j & 3;
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[I % (kPrefetch + 1)], p_operand(pk, s4),
                                                          oacc[db], 0, 0, 0);
-      if constexpr ((j & 3) == 0) {
-        sl.ld.template store_one<j / 4>(sl.sk, sl.sv, sl.tid);
-        sl.ld.template load_one<j / 4>(sl.rk, sl.rv, sl.krow, sl.vrow, sl.kload, sl.tid);
+      if constexpr (LOADS) {
+        constexpr int CH = TileLoader<NT>::CH, every = 16 / CH;
+        if constexpr (j % every == 0) {
+          sl.ld.template store_one<j / every>(sl.sk, sl.sv, sl.tid);
+          sl.ld.template load_one<j / every>(sl.rk, sl.rv, sl.krow, sl.vrow, sl.kload, sl.tid);
+        }
       }
     }
-    step_body<I + 1, NT>(sacc, oacc, qf, pk, sK, sV, l32, h, lane, fr, sl);
+    step_body<I + 1, FIRST, LAST, LOADS, NT>(sacc, oacc, qf, pk, sK, sV, l32, h, lane, fr, sl);
   }
 }
 
-template <int I>
+template <int I, int LAST, bool LOADS, int CH>
 __device__ __forceinline__ void step_schedule() {
-  if constexpr (I < 32) {
-    if constexpr (I + kPrefetch < 32)
+  if constexpr (I < LAST) {
+    if constexpr (I + kPrefetch < LAST)
       __builtin_amdgcn_sched_group_barrier(0x100, I + kPrefetch < 16 ? 1 : 2, 0);   // LDS reads
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             // one MFMA
-    if constexpr (I >= 16 && ((I - 16) & 3) == 0) {
+    if constexpr (LOADS && I >= 16 && ((I - 16) % (16 / CH)) == 0) {
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                           // LDS store
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                           // global load
     }
-    step_schedule<I + 1>();
+    step_schedule<I + 1, LAST, LOADS, CH>();
   }
 }
 
+template <int FIRST, int LAST, bool LOADS, int NT>
+__device__ __forceinline__ void mfma_range(f32x16 (&sacc)[2], f32x16 (&oacc)[4], const bf16x8 (&qf)[8],
+                                           const uint32_t (&pk)[2][8], const __bf16* sK, const __bf16* sV,
+                                           int l32, int h, int lane, const StepLoads<NT>& sl) {
+  static_assert(LAST - FIRST >= kPrefetch && kPrefetch == 4, "prologue reads");
+  static_assert(16 % TileLoader<NT>::CH == 0, "staged chunks spread over the PV MFMAs");
+  if constexpr (FIRST == 0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+  }
+  bf16x8 fr[kPrefetch + 1];
+  fr[FIRST % (kPrefetch + 1)] = step_operand<FIRST>(sK, sV, l32, h, lane);
+  fr[(FIRST + 1) % (kPrefetch + 1)] = step_operand<FIRST + 1>(sK, sV, l32, h, lane);
+  fr[(FIRST + 2) % (kPrefetch + 1)] = step_operand<FIRST + 2>(sK, sV, l32, h, lane);
+  fr[(FIRST + 3) % (kPrefetch + 1)] = step_operand<FIRST + 3>(sK, sV, l32, h, lane);
+  step_body<FIRST, FIRST, LAST, LOADS, NT>(sacc, oacc, qf, pk, sK, sV, l32, h, lane, fr, sl);
+  __builtin_amdgcn_sched_group_barrier(0x100, (FIRST < 16 ? 1 : 2) * kPrefetch, 0);
+  step_schedule<FIRST, LAST, LOADS, TileLoader<NT>::CH>();
+}
+
+// One MFMA phase of the dense pipeline: QK^T of the next tile and PV of the
+// current one, with the staging of the tile after next riding on the PV.
 template <int NT>
 __device__ __forceinline__ void mfma_step(f32x16 (&sacc)[2], f32x16 (&oacc)[4], const bf16x8 (&qf)[8],
                                           const uint32_t (&pk)[2][8], const __bf16* sK, const __bf16* sV,
                                           int l32, int h, int lane, const StepLoads<NT>& sl) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-  bf16x8 fr[kPrefetch + 1];
-  fr[0] = step_operand<0>(sK, sV, l32, h, lane);
-  fr[1] = step_operand<1>(sK, sV, l32, h, lane);
-  fr[2] = step_operand<2>(sK, sV, l32, h, lane);
-  fr[3] = step_operand<3>(sK, sV, l32, h, lane);
-  static_assert(kPrefetch == 4, "prologue reads");
-  static_assert(TileLoader<NT>::CH == 4, "one staged chunk per PV k-step");
-  step_body<0, NT>(sacc, oacc, qf, pk, sK, sV, l32, h, lane, fr, sl);
-  __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);
-  step_schedule<0>();
+  mfma_range<0, 32, true, NT>(sacc, oacc, qf, pk, sK, sV, l32, h, lane, sl);
 }
 
 __device__ __forceinline__ void mask_tail(f32x16 (&sacc)[2], int key0, int N, int h) {
@@ -520,7 +537,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       ld.load(rk, rv, krow, vrow, k0, tid);
       ld.store(smK[0], smV[0], tid);
       k1 = tiles.next();
-      if (k1 >= 0) ld.load(rk, rv, krow, vrow, k1, tid);
+      ld.load(rk, rv, krow, vrow, k1 >= 0 ? k1 : N, tid);
     }
     __syncthreads();
 
@@ -529,16 +546,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     int kc = k0, kn = k1, bc = 0;
     bool first = true;   // wave-uniform
     while (kc >= 0 && kc + BN <= N) {
-      qk_tile(sacc, smK[bc], qf, l32, h);
+      // The staged tile goes to the other buffer even when there is none
+      // (that buffer is free), and loads past the last tile fetch key offset
+      // N, which the buffer bounds turn into zeros.
+      const int kn2 = kn >= 0 ? tiles.next() : -1;
+      const StepLoads<NT> sl = {ld, smK[bc ^ 1], smV[bc ^ 1], rk, rv, krow, vrow, kn2 >= 0 ? kn2 : N, tid};
+      mfma_range<0, 16, false, NT>(sacc, oacc, qf, pk, smK[bc], smV[bc], l32, h, lane, sl);
       softmax_next(sacc, st, oacc, pk, c, first);
       first = false;
-      pv_tile(oacc, pk, smV[bc], lane);
-      int kn2 = -1;
-      if (kn >= 0) {
-        ld.store(smK[bc ^ 1], smV[bc ^ 1], tid);
-        kn2 = tiles.next();
-        if (kn2 >= 0) ld.load(rk, rv, krow, vrow, kn2, tid);
-      }
+      mfma_range<16, 32, true, NT>(sacc, oacc, qf, pk, smK[bc], smV[bc], l32, h, lane, sl);
       __syncthreads();
       kc = kn;
       kn = kn2;
