@@ -11,9 +11,11 @@ algorithmic TFLOP/s of that step (4 N^2 D flops per (b, h)).
 In the same run and on the same stream, timed the same way (W warm-ups, then
 K timed launches between HIP events), the other kernels of the path are
 reported as legs: the fp8 recipe (quantisation pass + fp8 attention) and the
-block-sparse kernel at the same 2048^2 shape with B=1, and the dense kernel at
-the 1024^2 shape.  The fp64 CPU oracle is timed on a bounded sample of rows
-of the same workload as the CPU baseline.
+block-sparse kernel at the same 2048^2 shape with B=1 (optionally the dense
+kernel at the 1024^2 and image-to-image shapes).  For the step, launch_stats
+adds per-launch min / median times and one cold-cache launch.  The fp64 CPU
+oracle is timed on a bounded sample of rows of the same workload as the CPU
+baseline.
 
 Prints ONE JSON line.
 """
@@ -53,6 +55,30 @@ def _time_launches(fn, steps, warmup, torch):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def _launch_stats(fn, steps, torch, flush_mib=512):
+    """Per-launch times (an event pair around each of `steps` launches, so a
+    little slower than the bracketed average) -> min and median, plus one
+    launch after a write of `flush_mib` MiB that evicts L2 and the
+    infinity cache (cold-cache time)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    ts = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    junk = torch.empty(flush_mib << 18, dtype=torch.float32, device="cuda")
+    junk.fill_(1.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    del junk
+    return {"min_ms": round(ts[0], 4), "median_ms": round(ts[len(ts) // 2], 4),
+            "cold_ms": round(e0.elapsed_time(e1), 4), "per_launch_samples": steps}
 
 
 def _source_sha(*names):
@@ -154,6 +180,8 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     sha = _source_sha("attn_bf16.hip", "device_common.h")
     traffic = _traffic("attn_bf16_img2048", sha)
+    stats = _launch_stats(lambda: dit.attn_fwd(qd, kd, vd, out=o), args.steps, torch)
+    log(f"[bench] {w.name}: per-launch {stats}")
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": "attn_bf16_kernel<8,3,false,false>",
@@ -252,7 +280,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": dict(w.describe(), softmax_scale="1/sqrt(128)", seed=0),
-        "roofline": roofline, "cpu_baseline": cpu, "legs": legs,
+        "roofline": roofline, "cpu_baseline": cpu, "launch_stats": stats, "legs": legs,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
