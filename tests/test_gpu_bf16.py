@@ -151,3 +151,19 @@ def test_img2048_cfg_pair_sampled_parity():
 def test_i2i2048_sampled_parity():
     """Image-to-image joint sequence: text + target + reference latents."""
     _sampled_parity("i2i2048", 256)
+
+
+def test_long_sequence_sampled_parity():
+    """One head of 2^20 + 37 tokens: byte offsets far past 2^24 inside the
+    slice, 16385 key tiles with a ragged last one."""
+    N = (1 << 20) + 37
+    _say(f"case: long sequence B1 H1 N{N}")
+    q, k, v = make_qkv(1, 1, N, 128, seed=31)
+    o32 = dit.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), out_fp32=True)
+    torch.cuda.synchronize()
+    rows = torch.unique(torch.cat([torch.tensor([0, 1, N // 2, N - 38, N - 37, N - 1]),
+                                   torch.randint(0, N, (26,), generator=torch.Generator().manual_seed(32))]))
+    ref, _ = oracle.attn(q, k, v, 1.0 / math.sqrt(128), rows=rows)
+    e = errors(o32.reshape(-1, 128)[rows.to(DEV)].cpu(), ref)
+    _say(f"fp32-out {e}")
+    assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e

@@ -135,3 +135,20 @@ def test_img2048_sparse_sampled_parity():
     _say(f"sparse fp32-out {e}")
     assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
     assert bf16_elementwise_ok(o16.reshape(-1, 128)[rows.to(DEV)].cpu(), ref).all()
+
+
+def test_long_sequence_sparse_sampled_parity():
+    """One head of 2^19 + 77 tokens (4097 mask blocks, ragged last block),
+    density 0.02 plus the forced diagonal and first block."""
+    N = (1 << 19) + 77
+    _say(f"case: long sequence block-sparse B1 H1 N{N}")
+    q, k, v = make_qkv(1, 1, N, 128, seed=91)
+    mask = make_block_mask(N, 64, 0.02, seed=92)
+    o32 = dit.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), mask.to(DEV), out_fp32=True)
+    torch.cuda.synchronize()
+    rows = torch.unique(torch.cat([torch.tensor([0, 127, 128, N // 2, N - 78, N - 77, N - 1]),
+                                   torch.randint(0, N, (25,), generator=torch.Generator().manual_seed(93))]))
+    ref, _ = oracle.attn(q, k, v, 1.0 / math.sqrt(128), mask=mask, rows=rows)
+    e = errors(o32.reshape(-1, 128)[rows.to(DEV)].cpu(), ref)
+    _say(f"fp32-out {e}")
+    assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
