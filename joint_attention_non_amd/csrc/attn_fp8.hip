@@ -10,7 +10,10 @@
 //   into LDS without any shuffle.
 //
 // Attention (work-group = 8 waves x 32 query rows, two waves per SIMD; key
-// tiles of 128 = one scale block), per tile with the 32x32x64 f8f6f4 MFMA:
+// tiles of 128 = one scale block, in three rotating LDS buffers; the QK^T
+// MFMAs of tile t+1 and the PV MFMAs of tile t form one stream with their
+// LDS operands read ahead, then one barrier, then the softmax of tile t+1),
+// per tile with the 32x32x64 f8f6f4 MFMA:
 //   S^T = K8 Q8^T                    raw integer-grid dot products (fp32)
 //   t = S * (sQ sK scale log2 e)     logits in log2 units
 //   m' = max(m, rowmax t), alpha = 2^(m - m')
@@ -138,14 +141,196 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(Fp8Args a) {
 
 constexpr int BN8 = 128;        // keys per tile = one scale block
 constexpr int RS8 = 128 + 16;   // LDS row stride in bytes (conflict-free 16-byte reads)
+constexpr int NB8 = 3;          // rotating LDS tile buffers
+constexpr int kPre8 = 2;        // MFMA operands read this many MFMAs ahead
 
-template <int NW, int R, bool OUT_F32>
-__global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_fp8_kernel(Fp8Args a, int nqb) {
-  constexpr int BM = NW * 32 * R, NT = NW * 64;
-  constexpr int KCH = BN8 * (D / 16) / NT;   // 16-byte chunks of each of K8 and V8t per thread
+__device__ __forceinline__ i32x8 lds_frag8(const uint8_t* p) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(p), hi = *reinterpret_cast<const u32x4*>(p + 16);
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// A operand J of a step's MFMA stream.  J < 8: K8 fragment (s, kb) =
+// (J / 4, J % 4) of the next tile: rows 32 kb + l32, bytes 64 s + 32 h ..
+// +31.  J >= 8: V8t fragment (s, db) = ((J-8) / 4, (J-8) % 4) of the current
+// tile: d rows 32 db + l32, key bytes 64 s + 32 h .. +31.
+template <int J>
+__device__ __forceinline__ i32x8 op8(const uint8_t* sK, const uint8_t* sV, int l32, int h) {
+  if constexpr (J < 8) return lds_frag8(sK + ((J & 3) * 32 + l32) * RS8 + 64 * (J >> 2) + 32 * h);
+  else return lds_frag8(sV + (((J - 8) & 3) * 32 + l32) * RS8 + 64 * ((J - 8) >> 2) + 32 * h);
+}
+
+__device__ __forceinline__ i32x8 p_frag8(const uint32_t (&p8)[2][8], int s) {
+  return i32x8{(int)p8[s][0], (int)p8[s][1], (int)p8[s][2], (int)p8[s][3],
+               (int)p8[s][4], (int)p8[s][5], (int)p8[s][6], (int)p8[s][7]};
+}
+
+// Global -> register -> LDS staging of one 128-key tile of K8 (row-major)
+// and V8t (d-major), 16-byte chunks, KCH of each per thread.
+template <int NT>
+struct Loader8 {
+  static constexpr int KCH = BN8 * (D / 16) / NT;
   static_assert(KCH * NT == BN8 * (D / 16), "tile split");
-  __shared__ __attribute__((aligned(16))) uint8_t smK[2][BN8 * RS8];
-  __shared__ __attribute__((aligned(16))) uint8_t smV[2][D * RS8];
+  u32x4 r[2 * KCH];
+  template <int I>
+  __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int t, int np,
+                                           int tid) {
+    const int id = tid + (I % KCH) * NT, row = id >> 3, c = id & 7;
+    if constexpr (I < KCH) r[I] = buf_load_b128(rk, (uint32_t)(t * BN8 + row) * D + c * 16);
+    else r[I] = buf_load_b128(rv, (uint32_t)row * np + t * BN8 + c * 16);
+  }
+  template <int I>
+  __device__ __forceinline__ void store_one(uint8_t* sk, uint8_t* sv, int tid) const {
+    const int id = tid + (I % KCH) * NT, row = id >> 3, c = id & 7;
+    *reinterpret_cast<u32x4*>((I < KCH ? sk : sv) + row * RS8 + c * 16) = r[I];
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int t, int np, int tid) {
+    if constexpr (KCH == 2) {
+      load_one<0>(rk, rv, t, np, tid); load_one<1>(rk, rv, t, np, tid);
+      load_one<2>(rk, rv, t, np, tid); load_one<3>(rk, rv, t, np, tid);
+    } else {
+      static_assert(KCH == 2, "loader unrolled for 512 threads");
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* sk, uint8_t* sv, int tid) const {
+    store_one<0>(sk, sv, tid); store_one<1>(sk, sv, tid);
+    store_one<2>(sk, sv, tid); store_one<3>(sk, sv, tid);
+  }
+};
+
+// MFMA I (0..15) of a step: 0-7 QK^T of the next tile, 8-15 PV of the
+// current one (plus, at I = 8 and 12, the row-sum MFMA of that 64-key step
+// with an all-ones A operand: every row of its result is the column sum of
+// P8, so each lane gets its query row's sum).  The four staged chunks are
+// stored to LDS and refilled from memory beside the PV MFMAs.
+template <int I, int NT>
+__device__ __forceinline__ void step8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f32x16& lacc, const i32x8 (&qf)[2],
+                                      const uint32_t (&p8)[2][8], const uint8_t* sK, const uint8_t* sV, int l32,
+                                      int h, i32x8 (&fr)[kPre8 + 1], Loader8<NT>& ld, uint8_t* sks, uint8_t* svs,
+                                      __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int tload, int np,
+                                      int tid) {
+  if constexpr (I < 16) {
+    if constexpr (I + kPre8 < 16) fr[(I + kPre8) % (kPre8 + 1)] = op8<I + kPre8>(sK, sV, l32, h);
+    const i32x8 a = fr[I % (kPre8 + 1)];
+    if constexpr (I < 8) {
+      constexpr int s = I >> 2, kb = I & 3;
+      sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[s], sacc[kb], 0, 0, 0, 0, 0, 0);
+    } else {
+      constexpr int s = (I - 8) >> 2, db = (I - 8) & 3;
+      const i32x8 pf = p_frag8(p8, s);
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, oacc[db], 0, 0, 0, 0, 0, 0);
+      if constexpr (db == 0) {
+        const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                            0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
+        lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, 0, 0, 0);
+      }
+      if constexpr ((I & 1) == 0) {
+        ld.template store_one<((I - 8) >> 1)>(sks, svs, tid);
+        ld.template load_one<((I - 8) >> 1)>(rk, rv, tload, np, tid);
+      }
+    }
+    step8<I + 1, NT>(sacc, oacc, lacc, qf, p8, sK, sV, l32, h, fr, ld, sks, svs, rk, rv, tload, np, tid);
+  }
+}
+
+template <int I>
+__device__ __forceinline__ void step8_schedule() {
+  if constexpr (I < 16) {
+    if constexpr (I + kPre8 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, ((I >= 8) && ((I - 8) & 3) == 0) ? 2 : 1, 0);
+    if constexpr (I >= 8 && (I & 1) == 0) {
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS store
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+    }
+    step8_schedule<I + 1>();
+  }
+}
+
+__device__ __forceinline__ void qk8_tile(f32x16 (&sacc)[4], const uint8_t* sK, const i32x8 (&qf)[2], int l32, int h) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          lds_frag8(sK + (kb * 32 + l32) * RS8 + 64 * s + 32 * h), qf[s], sacc[kb], 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void pv8_tile(f32x16 (&oacc)[4], f32x16& lacc, const uint32_t (&p8)[2][8],
+                                         const uint8_t* sV, int l32, int h) {
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const i32x8 pf = p_frag8(p8, s);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          lds_frag8(sV + (db * 32 + l32) * RS8 + 64 * s + 32 * h), pf, oacc[db], 0, 0, 0, 0, 0, 0);
+    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, 0, 0, 0);
+  }
+}
+
+// Softmax of one tile (keys key0 ..): t = S f, new running max, quantised
+// weights e4m3(2^(t - m + log2 448)) into p8, and the running accumulator
+// and row sum brought to the new max and to this tile's V scale.
+__device__ __forceinline__ void softmax8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f32x16& lacc, uint32_t (&p8)[2][8],
+                                         float& m_run, float& sv_prev, float f, float svt, float p_off, int key0,
+                                         int N, int h) {
+  if (key0 + BN8 > N) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+        if (key >= N) sacc[kb][r] = -INFINITY;
+      }
+  }
+  const float vratio = sv_prev / svt;
+  sv_prev = svt;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+  mx = fmaxf(mx, swap_halves(mx));
+  const float mnew = fmaxf(m_run, mx * f);
+  const float alpha = fast_exp2(m_run - mnew);
+  const float moff = mnew - p_off;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int slot = 4 * w + e, kb = 2 * s + (slot >> 4), r = slot & 15;
+        y[e] = fast_exp2(__builtin_fmaf(sacc[kb][r], f, -moff));
+      }
+      p8[s][w] = cvt4_e4m3(y[0], y[1], y[2], y[3]);
+    }
+  // Only element 0 of the row-sum accumulator is read at the end.
+  lacc[0] *= alpha;
+  m_run = mnew;
+  const float g = alpha * vratio;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] *= g;
+}
+
+// Work-group: NW waves x 32 query rows.  Step t issues the QK^T MFMAs of
+// tile t+1 and the PV MFMAs of tile t as one stream, their A operands read
+// from LDS kPre8 MFMAs ahead, with tile t+2 stored to LDS and tile t+3
+// loaded into registers beside the PV half; one barrier; then the softmax of
+// tile t+1.  Tiles rotate through NB8 LDS buffers.
+template <int NW, bool OUT_F32>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb) {
+  constexpr int BM = NW * 32, NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) uint8_t smK[NB8][BN8 * RS8];
+  __shared__ __attribute__((aligned(16))) uint8_t smV[NB8][D * RS8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -161,199 +346,94 @@ __global__ __launch_bounds__(NW * 64, (R == 1 ? 2 : 1)) void attn_fp8_kernel(Fp8
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k8, (uint32_t)(np * D));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v8, (uint32_t)(np * D));
 
-  const int q0 = qblk * BM + wave * 32 * R;
+  const int q0 = qblk * BM + wave * 32;
   const float sqw = (q0 < np) ? a.sq[(int64_t)bh * nb + q0 / kBlock] : 1.f;
   const float fq = sqw * a.c;
+  const float* skp = a.sk + (int64_t)bh * nb;
+  const float* svp = a.sv + (int64_t)bh * nb;
 
-  // Q8 as the B operand: lane (l32, h) holds row q0 + 32 qi + l32, d = 64 s + 32 h .. +31.
-  i32x8 qf[R][2];
+  // Q8 as the B operand: lane (l32, h) holds row q0 + l32, d = 64 s + 32 h .. +31.
+  i32x8 qf[2];
 #pragma unroll
-  for (int qi = 0; qi < R; ++qi)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint32_t off = (uint32_t)(q0 + qi * 32 + l32) * D + 64 * s + 32 * h;
-      const u32x4 lo = buf_load_b128(rq, off), hi = buf_load_b128(rq, off + 16);
-      qf[qi][s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
-
-  f32x16 oacc[R][4];
-#pragma unroll
-  for (int qi = 0; qi < R; ++qi)
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qi][db][r] = 0.f;
-  float m_run[R];
-  f32x16 lacc[R];   // row sums of the quantised weights (448 units), element 0 used
-#pragma unroll
-  for (int qi = 0; qi < R; ++qi) {
-    m_run[qi] = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) lacc[qi][r] = 0.f;
+  for (int s = 0; s < 2; ++s) {
+    const uint32_t off = (uint32_t)(q0 + l32) * D + 64 * s + 32 * h;
+    const u32x4 lo = buf_load_b128(rq, off), hi = buf_load_b128(rq, off + 16);
+    qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
-  const i32x8 kOnes = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                       0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
-  float sv_prev = 1.f;
 
-  // tile loader: KCH x 16 B of K8 and of V8t per thread
-  u32x4 kr[KCH], vr[KCH];
-  auto load_tile = [&](int t) {
+  f32x16 oacc[4];
+  f32x16 lacc;   // row sums of the quantised weights (448 units), element 0 used
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + i * NT, row = id >> 3, c = id & 7;
-      kr[i] = buf_load_b128(rk, (uint32_t)(t * BN8 + row) * D + c * 16);
-      vr[i] = buf_load_b128(rv, (uint32_t)row * np + t * BN8 + c * 16);
-    }
-  };
-  auto store_tile = [&](int bf) {
+  for (int r = 0; r < 16; ++r) {
+    lacc[r] = 0.f;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + i * NT, row = id >> 3, c = id & 7;
-      *reinterpret_cast<u32x4*>(&smK[bf][row * RS8 + c * 16]) = kr[i];
-      *reinterpret_cast<u32x4*>(&smV[bf][row * RS8 + c * 16]) = vr[i];
-    }
-  };
+    for (int db = 0; db < 4; ++db) oacc[db][r] = 0.f;
+  }
+  float m_run = -INFINITY, sv_prev = 1.f;
 
-  load_tile(0);
-  store_tile(0);
-  if (nb > 1) load_tile(1);
+  // ---- prologue: tiles 0 and 1 into LDS, tile 2 into registers ----
+  Loader8<NT> ld;
+  ld.load(rk, rv, 0, np, tid);
+  ld.store(smK[0], smV[0], tid);
+  ld.load(rk, rv, min(1, nb - 1), np, tid);
+  ld.store(smK[1], smV[1], tid);
+  ld.load(rk, rv, min(2, nb - 1), np, tid);
   __syncthreads();
 
-  for (int t = 0; t < nb; ++t) {
-    const int bf = t & 1;
-    const uint8_t* sK = smK[bf];
-    const uint8_t* sV = smV[bf];
-    const int key0 = t * BN8;
+  f32x16 sacc[4];
+  uint32_t p8[2][8];
+  qk8_tile(sacc, smK[0], qf, l32, h);
+  softmax8(sacc, oacc, lacc, p8, m_run, sv_prev, fq * skp[0], svp[0], a.p_off, 0, N, h);
 
-    // ---- S^T = K8 Q8^T ----
-    f32x16 sacc[R][4];
+  int bc = 0;   // LDS buffer of tile t; tile t+1 is in bc+1, tile t+2 goes to bc+2 (mod 3)
+  for (int t = 0; t + 1 < nb; ++t) {
+    const int bn = (bc + 1 == NB8) ? 0 : bc + 1;
+    const int bn2 = (bn + 1 == NB8) ? 0 : bn + 1;
+    // Past the last tile the staged buffer is free and never read, and the
+    // load repeats the last tile.
+    const int tload = min(t + 3, nb - 1);
 #pragma unroll
-    for (int qi = 0; qi < R; ++qi)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qi][kb][r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint8_t* p = sK + (kb * 32 + l32) * RS8 + 64 * s + 32 * h;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(p), hi = *reinterpret_cast<const u32x4*>(p + 16);
-        const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-#pragma unroll
-        for (int qi = 0; qi < R; ++qi)
-          sacc[qi][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[qi][s], sacc[qi][kb], 0, 0, 0, 0, 0, 0);
-      }
-
-    if (key0 + BN8 > N) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (key >= N) {
-#pragma unroll
-            for (int qi = 0; qi < R; ++qi) sacc[qi][kb][r] = -INFINITY;
-          }
-        }
-    }
-
-    const float f = fq * a.sk[(int64_t)bh * nb + t];
-    const float svt = a.sv[(int64_t)bh * nb + t];
-    const float vratio = sv_prev / svt;
-    sv_prev = svt;
-
-    uint32_t p8[R][2][8];   // [qi][k-step of 64 keys][dword]
-#pragma unroll
-    for (int qi = 0; qi < R; ++qi) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qi][kb][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float mnew = fmaxf(m_run[qi], mx * f);
-      const float alpha = fast_exp2(m_run[qi] - mnew);
-      const float moff = mnew - a.p_off;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int slot = 4 * w + e, kb = 2 * s + (slot >> 4), r = slot & 15;
-            y[e] = fast_exp2(__builtin_fmaf(sacc[qi][kb][r], f, -moff));
-          }
-          p8[qi][s][w] = cvt4_e4m3(y[0], y[1], y[2], y[3]);
-        }
-      // Only element 0 of the row-sum accumulator is read (see below).
-      lacc[qi][0] *= alpha;
-      m_run[qi] = mnew;
-      const float g = alpha * vratio;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[qi][db][r] *= g;
-    }
-
-    // ---- A += V8^T P8^T ----
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint8_t* p = sV + (db * 32 + l32) * RS8 + 64 * s + 32 * h;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(p), hi = *reinterpret_cast<const u32x4*>(p + 16);
-        const i32x8 vf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-#pragma unroll
-        for (int qi = 0; qi < R; ++qi) {
-          const i32x8 pf = {(int)p8[qi][s][0], (int)p8[qi][s][1], (int)p8[qi][s][2], (int)p8[qi][s][3],
-                            (int)p8[qi][s][4], (int)p8[qi][s][5], (int)p8[qi][s][6], (int)p8[qi][s][7]};
-          oacc[qi][db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, oacc[qi][db], 0, 0, 0, 0, 0, 0);
-          // Row sum of the quantised weights on the matrix core: an all-ones
-          // A operand makes every row of the 32x32 result the column sum of
-          // P8, so each lane gets its query row's sum in every register.
-          if (db == 0)
-            lacc[qi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kOnes, pf, lacc[qi], 0, 0, 0, 0, 0, 0);
-        }
-      }
-
-    if (t + 1 < nb) {
-      store_tile(bf ^ 1);
-      if (t + 2 < nb) load_tile(t + 2);
-    }
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    i32x8 fr[kPre8 + 1];
+    fr[0] = op8<0>(smK[bn], smV[bc], l32, h);
+    fr[1] = op8<1>(smK[bn], smV[bc], l32, h);
+    step8<0, NT>(sacc, oacc, lacc, qf, p8, smK[bn], smV[bc], l32, h, fr, ld, smK[bn2], smV[bn2], rk, rv, tload,
+                 np, tid);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre8, 0);
+    step8_schedule<0>();
     __syncthreads();
+    softmax8(sacc, oacc, lacc, p8, m_run, sv_prev, fq * skp[t + 1], svp[t + 1], a.p_off, (t + 1) * BN8, N, h);
+    bc = bn;
   }
+  pv8_tile(oacc, lacc, p8, smV[bc], l32, h);
 
   // ---- epilogue: O = A * sV_last / l ----
   const int64_t ob = b * a.os[0] + hd * a.os[1];
+  const float lt = lacc[0];
+  const float inv = lt > 0.f ? sv_prev / lt : 0.f;
+  const int row = q0 + l32;
+  if (row < N) {
+    const int64_t orow = ob + (int64_t)row * a.os[2];
 #pragma unroll
-  for (int qi = 0; qi < R; ++qi) {
-    const float lt = lacc[qi][0];
-    const float inv = lt > 0.f ? sv_prev / lt : 0.f;
-    const int row = q0 + qi * 32 + l32;
-    if (row < N) {
-      const int64_t orow = ob + (int64_t)row * a.os[2];
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = db * 32 + r4 * 8 + h * 4;
-          const float v0 = oacc[qi][db][4 * r4 + 0] * inv, v1 = oacc[qi][db][4 * r4 + 1] * inv;
-          const float v2 = oacc[qi][db][4 * r4 + 2] * inv, v3 = oacc[qi][db][4 * r4 + 3] * inv;
-          if constexpr (OUT_F32) {
-            f32x4 t4 = {v0, v1, v2, v3};
-            *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d0) = t4;
-          } else {
-            u32x2 t2 = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + orow + d0) = t2;
-          }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + r4 * 8 + h * 4;
+        const float v0 = oacc[db][4 * r4 + 0] * inv, v1 = oacc[db][4 * r4 + 1] * inv;
+        const float v2 = oacc[db][4 * r4 + 2] * inv, v3 = oacc[db][4 * r4 + 3] * inv;
+        if constexpr (OUT_F32) {
+          f32x4 t4 = {v0, v1, v2, v3};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d0) = t4;
+        } else {
+          u32x2 t2 = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + orow + d0) = t2;
         }
-      if (a.lse != nullptr && h == 0)
-        a.lse[(int64_t)bh * N + row] =
-            lt > 0.f ? (m_run[qi] + __builtin_log2f(lt) - 8.8073549220576041f) * 0.69314718055994530942f
-                     : -INFINITY;
-    }
+      }
+    if (a.lse != nullptr && h == 0)
+      a.lse[(int64_t)bh * N + row] =
+          lt > 0.f ? (m_run + __builtin_log2f(lt) - 8.8073549220576041f) * 0.69314718055994530942f : -INFINITY;
   }
 }
 
@@ -370,8 +450,8 @@ hipError_t launch_attn_fp8(const Fp8Args& a, bool out_f32, hipStream_t s) {
   const int nqb = (a.N + 255) / 256;   // 8 waves x 32 query rows per work-group
   const int64_t nwg = (int64_t)a.B * a.H * nqb;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (out_f32) hipLaunchKernelGGL((attn_fp8_kernel<8, 1, true>), dim3((unsigned)nwg), dim3(512), 0, s, a, nqb);
-  else hipLaunchKernelGGL((attn_fp8_kernel<8, 1, false>), dim3((unsigned)nwg), dim3(512), 0, s, a, nqb);
+  if (out_f32) hipLaunchKernelGGL((attn_fp8_kernel<8, true>), dim3((unsigned)nwg), dim3(512), 0, s, a, nqb);
+  else hipLaunchKernelGGL((attn_fp8_kernel<8, false>), dim3((unsigned)nwg), dim3(512), 0, s, a, nqb);
   return hipGetLastError();
 }
 
