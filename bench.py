@@ -3,10 +3,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--legs all|none]
 
 A step is one dense bf16 joint-attention forward (QK^T, online softmax, PV,
-epilogue -- the whole hot path of dit_attn_fwd) over the 2048x2048-image DiT
-shape with its CFG pair: B=2, H=24, N=512 text + 16384 image = 16896 tokens,
-D=128, 1% of key rows x8 (inputs already resident in HBM).  `value` is the
-algorithmic TFLOP/s of that step (4 N^2 D flops per (b, h)).
+epilogue -- the whole hot path of dit_attn_fwd_ws: the attention kernel and,
+for the query blocks of its last partial round, the merge of their split key
+ranges) over the 2048x2048-image DiT shape with its CFG pair: B=2, H=24,
+N=512 text + 16384 image = 16896 tokens, D=128, 1% of key rows x8 (inputs
+already resident in HBM).  `value` is the algorithmic TFLOP/s of that step
+(4 N^2 D flops per (b, h)).  The same forward without the split
+(dit_attn_fwd) is timed beside it as `ms_no_split`.
 
 In the same run and on the same stream, timed the same way (W warm-ups, then
 K timed launches between HIP events), the other kernels of the path are
@@ -173,21 +176,27 @@ def main():
     q, k, v, _ = make_workload_inputs(w, seed=0)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     o = torch.empty_like(qd)
-    log(f"[bench] timing {w.name}: warmup {args.warmup}, steps {args.steps}")
+    wsb = dit.fwd_workspace(qd)
+    log(f"[bench] timing {w.name}: warmup {args.warmup}, steps {args.steps}, "
+        f"tail-split workspace {dit.fwd_workspace_bytes(qd)} bytes")
     torch.cuda.synchronize()
-    ms = _time_launches(lambda: dit.attn_fwd(qd, kd, vd, out=o), args.steps, args.warmup, torch)
+    step = lambda: dit.attn_fwd(qd, kd, vd, out=o, workspace=wsb)
+    ms = _time_launches(step, args.steps, args.warmup, torch)
+    ms_plain = _time_launches(lambda: dit.attn_fwd(qd, kd, vd, out=o), args.steps, args.warmup, torch)
     flops = _flops_dense(w.batch, w.heads, w.seqlen, w.head_dim)
     tflops = flops / (ms * 1e-3) / 1e12
     sha = _source_sha("attn_bf16.hip", "device_common.h")
     traffic = _traffic("attn_bf16_img2048", sha)
-    stats = _launch_stats(lambda: dit.attn_fwd(qd, kd, vd, out=o), args.steps, torch)
+    stats = _launch_stats(step, args.steps, torch)
+    stats["ms_no_split"] = round(ms_plain, 4)
     log(f"[bench] {w.name}: per-launch {stats}")
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": "attn_bf16_kernel<8,3,false,false>",
                 "flops_per_launch": flops}
-    log(f"[bench] {w.name}: {ms:.3f} ms  {tflops:.1f} TFLOP/s  {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
-    del o
+    log(f"[bench] {w.name}: {ms:.3f} ms  {tflops:.1f} TFLOP/s  {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak"
+        f"  (without the tail split {ms_plain:.3f} ms)")
+    del o, wsb
 
     legs = {}
     if args.legs == "all":
@@ -249,14 +258,15 @@ def main():
         q1, k1, v1, _ = make_workload_inputs(w1, seed=0)
         q1, k1, v1 = (t.to(dev) for t in (q1, k1, v1))
         o1 = torch.empty_like(q1)
-        ms_1 = _time_launches(lambda: dit.attn_fwd(q1, k1, v1, out=o1),
+        ws1 = dit.fwd_workspace(q1)
+        ms_1 = _time_launches(lambda: dit.attn_fwd(q1, k1, v1, out=o1, workspace=ws1),
                               max(args.steps, 50) if w1.seqlen < 8192 else args.steps,
                               args.warmup, torch)
         f1 = _flops_dense(w1.batch, w1.heads, w1.seqlen, w1.head_dim)
         legs[w1.name] = {"ms": round(ms_1, 4), "achieved": round(f1 / (ms_1 * 1e-3) / 1e12, 2),
                          "unit": "TFLOP/s", "frac": round(f1 / (ms_1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         log(f"[bench] {w1.name}: {legs[w1.name]}")
-        del q1, k1, v1, o1
+        del q1, k1, v1, o1, ws1
 
     if args.calib_copy:
         n = args.calib_copy * (1 << 20) // 4

@@ -82,6 +82,30 @@ int dit_attn_fwd(const dit_attn_shape* shape,
                  const void* q, const void* k, const void* v,
                  void* o, float* lse, void* stream);
 
+/* Workspace bytes dit_attn_fwd_ws needs for `shape` on the current device
+ * (0: no split applies, the workspace may be NULL; also 0 for an invalid
+ * shape).  Layout: fp32 [P][256][132], one row per query row of each of the
+ * P = ntail * split tail work-groups: 128 unnormalised O values, m * scale
+ * * log2(e), the row's weight sum, 2 words of padding. */
+size_t dit_attn_fwd_workspace_bytes(const dit_attn_shape* shape);
+
+/* The same attention as dit_attn_fwd (same operation, same arguments and
+ * errors), with a caller workspace for load balancing: the query blocks of
+ * 256 rows run one per compute unit, and those of the last, partial round
+ * are each split into key ranges whose partial results (own running max,
+ * unnormalised O and weight sum) are combined by a second kernel in key
+ * order: O = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p with M = max m_p.
+ * The workspace (device memory, 256-byte aligned, caller-owned, at least
+ * dit_attn_fwd_workspace_bytes) is scratch: nothing is read from it before
+ * it is written in the same call; calls that share one workspace must not
+ * overlap.  Output is deterministic per device; rows of split blocks can
+ * differ from dit_attn_fwd's in the last bits (P is rounded against a
+ * different reference max). */
+int dit_attn_fwd_ws(const dit_attn_shape* shape,
+                    const void* q, const void* k, const void* v,
+                    void* o, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes dit_attn_fwd_fp8 / dit_attn_fp8_quantize need for `shape`
  * (0 if the shape is invalid).  Layout, with BH = B*H, nb = ceil(N/128),
  * Np = 128*nb, each region starting at a 256-byte boundary in this order:

@@ -5,7 +5,7 @@ kernels of ``libdit_attn.so``.  PyTorch supplies device memory and the
 current stream.  There is no fallback: if the library is not built, or a
 call fails, an exception is raised.
 
-    attn_fwd(q, k, v, scale=None, return_lse=False, out_fp32=False)
+    attn_fwd(q, k, v, scale=None, return_lse=False, out_fp32=False, workspace=None)
     attn_fwd_fp8(q, k, v, scale=None, return_lse=False, workspace=None, out_fp32=False)
     attn_fwd_blocksparse(q, k, v, block_mask, scale=None, return_lse=False, out_fp32=False)
     fp8_quantize(q, k, v, workspace=None) -> Fp8Workspace views
@@ -23,7 +23,8 @@ import os
 import torch
 
 __all__ = ["attn_fwd", "attn_fwd_fp8", "attn_fwd_blocksparse", "fp8_quantize",
-           "fp8_workspace_bytes", "DitAttnError", "library_path", "load"]
+           "fp8_workspace_bytes", "fwd_workspace_bytes", "fwd_workspace", "DitAttnError",
+           "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdit_attn.so")
@@ -61,6 +62,10 @@ def load():
         vp, sp = ctypes.c_void_p, ctypes.POINTER(_Shape)
         lib.dit_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         lib.dit_attn_fwd.restype = ctypes.c_int
+        lib.dit_attn_fwd_workspace_bytes.argtypes = [sp]
+        lib.dit_attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.dit_attn_fwd_ws.argtypes = [sp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.dit_attn_fwd_ws.restype = ctypes.c_int
         lib.dit_attn_fwd_fp8_workspace_bytes.argtypes = [sp]
         lib.dit_attn_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
         lib.dit_attn_fwd_fp8.argtypes = [sp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -126,13 +131,35 @@ def _outputs(q, return_lse, out_fp32, out=None):
     return out, lse
 
 
-def attn_fwd(q, k, v, scale=None, return_lse=False, out_fp32=False, out=None):
-    """Dense bf16 joint attention; returns O (and lse if asked)."""
+def fwd_workspace_bytes(q) -> int:
+    """Bytes of the tail-split workspace dit_attn_fwd_ws needs for q's shape
+    on the current device (0: no split applies)."""
+    B, H, N, D = q.shape
+    s = _Shape()
+    s.batch, s.heads, s.seqlen, s.head_dim = B, H, N, D
+    return int(load().dit_attn_fwd_workspace_bytes(ctypes.byref(s)))
+
+
+def attn_fwd(q, k, v, scale=None, return_lse=False, out_fp32=False, out=None, workspace=None):
+    """Dense bf16 joint attention; returns O (and lse if asked).  With a
+    workspace (uint8 device tensor of at least fwd_workspace_bytes(q) bytes)
+    the last partial round of query blocks is split over key ranges
+    (dit_attn_fwd_ws)."""
     o, lse = _outputs(q, return_lse, out_fp32, out)
     s = _shape(q, k, v, o, scale, FLAG_OUT_F32 if out_fp32 else 0)
-    _check(load().dit_attn_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                               _stream()), "dit_attn_fwd")
+    if workspace is None:
+        _check(load().dit_attn_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                   _stream()), "dit_attn_fwd")
+    else:
+        _check(load().dit_attn_fwd_ws(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream()), "dit_attn_fwd_ws")
     return (o, lse) if return_lse else o
+
+
+def fwd_workspace(q):
+    """A workspace tensor for attn_fwd(..., workspace=...) (at least 256 bytes)."""
+    return torch.empty(max(fwd_workspace_bytes(q), 256), dtype=torch.uint8, device=q.device)
 
 
 def attn_fwd_blocksparse(q, k, v, block_mask, scale=None, return_lse=False, out_fp32=False,

@@ -428,7 +428,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  // Work-group -> query block; a tail work-group (dense only) also gets one
+  // of the `split` key ranges of its block.
+  int tile, part = -1;
+  if ((int)blockIdx.x < a.nfull) {
+    tile = xcd_remap(blockIdx.x, a.nfull);
+  } else {
+    const int j = blockIdx.x - a.nfull;
+    tile = a.nfull + j / a.split;
+    part = j % a.split;
+  }
   const int bh = tile / a.nqb, qblk = tile % a.nqb;
   const int b = bh / a.H, hd = bh % a.H;
   const int N = a.N;
@@ -468,8 +477,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     tiles.pend = -1;
     tiles.bits = 0;
   } else {
-    tiles.pos = 0;
-    tiles.N = N;
+    // Key tiles [t0, t1) of nt for part p of `split`: t = p * nt / split.
+    int kbeg = 0, kend = N;
+    if (part >= 0) {
+      const int nt = (N + BN - 1) / BN;
+      kbeg = part * nt / a.split * BN;
+      kend = min((part + 1) * nt / a.split * BN, N);
+    }
+    tiles.pos = kbeg;
+    tiles.N = kend;
   }
 
   TileLoader<NT> ld;
@@ -573,6 +589,26 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   const float lt = row_sum_halves(st.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int row = q0 + l32;
+  if constexpr (!SPARSE) {
+    if (part >= 0) {
+      // Partial result of one key range: unnormalised O, m c and l.
+      float* pr = a.part + ((int64_t)(blockIdx.x - a.nfull) * BM + wave * 32 + l32) * kPartRow;
+      if (row < N) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 t = {oacc[db][4 * r4 + 0], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2], oacc[db][4 * r4 + 3]};
+            *reinterpret_cast<f32x4*>(pr + db * 32 + r4 * 8 + h * 4) = t;
+          }
+        if (h == 0) {
+          pr[128] = st.mc;
+          pr[129] = lt;
+        }
+      }
+      return;
+    }
+  }
   if (row < N) {
     const int64_t orow = ob + (int64_t)row * a.os[2];
 #pragma unroll
@@ -596,13 +632,66 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+// Combine the partial results of the split tail blocks, one wave per row:
+// M = max_p m_p c, w_p = 2^(m_p c - M), O = sum_p w_p O_p / sum_p w_p l_p,
+// lse = ln2 (M + log2 l), the parts taken in key order.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  const int rid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tail = rid / 256, rr = rid % 256;
+  const int tile = a.nfull + tail;
+  const int bh = tile / a.nqb, qblk = tile % a.nqb;
+  const int b = bh / a.H, hd = bh % a.H;
+  const int row = qblk * 256 + rr;
+  if (row >= a.N) return;
+  const float* base = a.part + ((int64_t)tail * a.split * 256 + rr) * kPartRow;
+  const int64_t pstride = (int64_t)256 * kPartRow;
+  float M = -INFINITY;
+  for (int p = 0; p < a.split; ++p) M = fmaxf(M, base[p * pstride + 128]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int p = 0; p < a.split; ++p) {
+    const float* pr = base + p * pstride;
+    const float w = fast_exp2(pr[128] - M);
+    L = __builtin_fmaf(w, pr[129], L);
+    const f32x2 ov = *reinterpret_cast<const f32x2*>(pr + 2 * lane);
+    o0 = __builtin_fmaf(w, ov[0], o0);
+    o1 = __builtin_fmaf(w, ov[1], o1);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int64_t orow = b * a.os[0] + hd * a.os[1] + (int64_t)row * a.os[2] + 2 * lane;
+  if constexpr (OUT_F32) {
+    const f32x2 t = {o0 * inv, o1 * inv};
+    *reinterpret_cast<f32x2*>(static_cast<float*>(a.o) + orow) = t;
+  } else {
+    *reinterpret_cast<uint32_t*>(static_cast<__bf16*>(a.o) + orow) = pack_bf16x2(o0 * inv, o1 * inv);
+  }
+  if (a.lse != nullptr && lane == 0)
+    a.lse[(int64_t)bh * a.N + row] = L > 0.f ? (M + __builtin_log2f(L)) * 0.69314718055994530942f : -INFINITY;
+}
+
 }  // namespace
+
+hipError_t launch_attn_merge(const AttnArgs& a, bool out_f32, hipStream_t s) {
+  if (a.split <= 1 || a.ntail <= 0) return hipSuccess;
+  const dim3 grid((unsigned)a.ntail * 64);
+  if (out_f32) hipLaunchKernelGGL((attn_merge_kernel<true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((attn_merge_kernel<false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_bf16(const AttnArgs& args, bool out_f32, bool sparse, hipStream_t s) {
   AttnArgs a = args;
   a.nqb = sparse ? a.nb : (a.N + 255) / 256;   // work-group rows: 128 (sparse) or 256 (dense)
-  const int64_t nwg = (int64_t)a.B * a.H * a.nqb;
+  int64_t nwg = (int64_t)a.B * a.H * a.nqb;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (sparse || a.split <= 1 || a.part == nullptr) {
+    a.nfull = (int)nwg;
+    a.ntail = 0;
+    a.split = 1;
+  } else {
+    if (a.nfull + a.ntail != nwg) return hipErrorInvalidConfiguration;
+    nwg = (int64_t)a.nfull + (int64_t)a.ntail * a.split;
+  }
   const dim3 grid((unsigned)nwg);
   if (sparse) {
     if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<4, 2, true, true>), grid, dim3(256), 0, s, a);
@@ -610,6 +699,9 @@ hipError_t launch_attn_bf16(const AttnArgs& args, bool out_f32, bool sparse, hip
   } else {
     if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<8, 3, true, false>), grid, dim3(512), 0, s, a);
     else hipLaunchKernelGGL((attn_bf16_kernel<8, 3, false, false>), grid, dim3(512), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_attn_merge(a, out_f32, s);
   }
   return hipGetLastError();
 }

@@ -2,6 +2,8 @@
 // layout and kernel dispatch.  Every check runs before the first HIP call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -102,6 +104,49 @@ int hip_status(hipError_t e, const char* what) {
   return fail(DIT_ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Compute units of the current device, read once per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64 && cus > 0) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Tail split of the dense bf16 grid: one 256-row work-group runs per CU at a
+// time, so B*H*ceil(N/256) work-groups leave a last partial round of r
+// blocks.  Each of those is split into `split` key ranges (as many as fill
+// the CUs, at most one per 64-key tile), so the last round costs 1/split of
+// a full one.  No split when there is no partial round or only one block
+// fits per CU.
+struct TailPlan {
+  int nfull = 0, ntail = 0, split = 1;
+  size_t bytes = 0;
+};
+
+TailPlan tail_plan(const dit_attn_shape* sh, int cus) {
+  TailPlan t;
+  const int64_t units = (int64_t)sh->batch * sh->heads * ((sh->seqlen + 255) / 256);
+  t.nfull = (int)units;
+  if (cus <= 0 || units > 0x7fffffff) return t;
+  const int64_t full_rounds = units / cus, r = units % cus;
+  const int64_t tiles = (sh->seqlen + 63) / 64;
+  if (full_rounds < 1 || r == 0) return t;
+  const int64_t split = std::min<int64_t>(cus / r, tiles);
+  if (split < 2) return t;
+  t.nfull = (int)(units - r);
+  t.ntail = (int)r;
+  t.split = (int)split;
+  t.bytes = (size_t)(r * split) * 256 * dit::kPartRow * sizeof(float);
+  return t;
+}
+
 struct Fp8Layout {
   size_t q8, k8, v8t, sq, sk, sv, total;
 };
@@ -194,6 +239,34 @@ int dit_attn_fwd(const dit_attn_shape* shape, const void* q, const void* k, cons
   return hip_status(dit::launch_attn_bf16(a, (shape->flags & DIT_ATTN_FLAG_OUT_F32) != 0, false,
                                           static_cast<hipStream_t>(stream)),
                     "dit_attn_fwd launch");
+}
+
+size_t dit_attn_fwd_workspace_bytes(const dit_attn_shape* shape) {
+  if (shape == nullptr || shape->batch < 1 || shape->heads < 1 || shape->seqlen < 1) return 0;
+  return tail_plan(shape, device_cus()).bytes;
+}
+
+int dit_attn_fwd_ws(const dit_attn_shape* shape, const void* q, const void* k, const void* v, void* o, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  int rc = check_common(shape, q, k, v, o, lse);
+  if (rc) return rc;
+  const TailPlan t = tail_plan(shape, device_cus());
+  dit::AttnArgs a;
+  fill_common(shape, q, k, v, o, lse, a);
+  if (t.split > 1) {
+    if (workspace == nullptr) return fail(DIT_ATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", t.bytes);
+    if (!aligned(workspace, 256)) return fail(DIT_ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < t.bytes)
+      return fail(DIT_ATTN_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, t.bytes);
+    a.nfull = t.nfull;
+    a.ntail = t.ntail;
+    a.split = t.split;
+    a.part = static_cast<float*>(workspace);
+  }
+  return hip_status(dit::launch_attn_bf16(a, (shape->flags & DIT_ATTN_FLAG_OUT_F32) != 0, false,
+                                          static_cast<hipStream_t>(stream)),
+                    "dit_attn_fwd_ws launch");
 }
 
 int dit_attn_fwd_blocksparse(const dit_attn_shape* shape, const void* q, const void* k, const void* v, void* o,

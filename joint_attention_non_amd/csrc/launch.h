@@ -21,7 +21,17 @@ struct AttnArgs {
   const uint8_t* mask;  // block-sparse only: [nb][nb] per (b, h)
   int64_t mask_bh;      // element offset between (b, h) masks
   int nb;               // ceil(N / 128)
+  // Dense tail balancing: work-groups [0, nfull) each own one query block
+  // and its whole key range; the last ntail query blocks are each split
+  // into `split` key ranges whose partial results go to `part` and are
+  // combined by the merge kernel.  split == 1: no tail split.
+  int nfull, ntail, split;
+  float* part;          // [ntail * split][256 rows][kPartRow] fp32
 };
+
+// fp32 words per row of a partial result: 128 unnormalised O, the row's
+// reference m c (log2 units), its weight sum l, and two words of padding.
+constexpr int kPartRow = 132;
 
 // Arguments of the fp8 quantisation pass and the fp8 attention kernel.
 struct Fp8Args {
@@ -44,6 +54,7 @@ struct Fp8Args {
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool out_f32, bool sparse, hipStream_t s);
+hipError_t launch_attn_merge(const AttnArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_fp8_quantize(const Fp8Args& a, hipStream_t s);
 hipError_t launch_attn_fp8(const Fp8Args& a, bool out_f32, hipStream_t s);
 

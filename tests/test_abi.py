@@ -23,7 +23,8 @@ def _declared():
 
 def test_header_declares_the_expected_calls():
     names = _declared()
-    for n in ("dit_attn_fwd", "dit_attn_fwd_fp8", "dit_attn_fwd_fp8_workspace_bytes",
+    for n in ("dit_attn_fwd", "dit_attn_fwd_ws", "dit_attn_fwd_workspace_bytes",
+              "dit_attn_fwd_fp8", "dit_attn_fwd_fp8_workspace_bytes",
               "dit_attn_fp8_quantize", "dit_attn_fwd_blocksparse", "dit_attn_status_string",
               "dit_attn_last_error", "dit_attn_version"):
         assert n in names
@@ -119,3 +120,23 @@ def test_status_strings():
     for st in range(0, 6):
         assert lib.dit_attn_status_string(st)
     assert lib.dit_attn_status_string(0).decode() == "ok"
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda s: setattr(s, "head_dim", 64), UNSUPPORTED),
+    (lambda s: setattr(s, "seqlen", 0), INVALID),
+    (lambda s: setattr(s, "softmax_scale", float("inf")), INVALID),
+    (lambda s: s.o_stride.__setitem__(2, 120), INVALID),
+])
+def test_fwd_ws_rejects_bad_shapes_before_any_device_call(mutate, status):
+    lib = dit.load()
+    s = _shape()
+    mutate(s)
+    assert lib.dit_attn_fwd_ws(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == status
+    assert lib.dit_attn_fwd_ws(None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == INVALID
+    assert lib.dit_attn_fwd_ws(ctypes.byref(_shape()), None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+                               None) == INVALID
+    assert lib.dit_attn_fwd_workspace_bytes(None) == 0
+    bad = _shape()
+    bad.seqlen = 0
+    assert lib.dit_attn_fwd_workspace_bytes(ctypes.byref(bad)) == 0
