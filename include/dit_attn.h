@@ -115,7 +115,12 @@ int dit_attn_fwd_ws(const dit_attn_shape* shape,
  *       every 64-key group the 4-key groups are stored in the order the PV
  *       operand is read: position group pg holds key group
  *       8*((pg>>2)&1) + 2*(pg&3) + (pg>>3); keys >= N are 0
- *   sQ, sK, sV  fp32 [BH][nb]  dequantisation scales (absmax / 448) */
+ *   sQ, sK, sV  fp32 [BH][nb]  dequantisation scales (absmax / 448)
+ *   part  fp32 [P][256][132]  scratch of the attention's tail split (see
+ *       dit_attn_fwd_ws; here in 128-key tiles, O already in V units, m in
+ *       log2 units, weights in units of 1/448); present only when the grid
+ *       leaves a partial round on the current device, so the size depends
+ *       on that device. */
 size_t dit_attn_fwd_fp8_workspace_bytes(const dit_attn_shape* shape);
 
 /* Quantised attention with on-device dynamic scaling.  FP8 dynamic
@@ -129,7 +134,10 @@ size_t dit_attn_fwd_fp8_workspace_bytes(const dit_attn_shape* shape);
  * product, and the row sum is taken over the same quantised weights (so the
  * normalised weights sum to one); output is bf16 (or fp32).
  * The quantisation pass writes the workspace (layout above), then the
- * attention pass reads it, both on `stream`. */
+ * attention pass reads it, both on `stream`.  As in dit_attn_fwd_ws, the
+ * 256-row query blocks of a last partial round are split over key ranges,
+ * each with its own running max, and merged with exact rescaling; their P
+ * is therefore rounded against a different running max than in one pass. */
 int dit_attn_fwd_fp8(const dit_attn_shape* shape,
                      const void* q, const void* k, const void* v,
                      void* o, float* lse,

@@ -633,8 +633,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 }
 
 // Combine the partial results of the split tail blocks, one wave per row:
-// M = max_p m_p c, w_p = 2^(m_p c - M), O = sum_p w_p O_p / sum_p w_p l_p,
-// lse = ln2 (M + log2 l), the parts taken in key order.
+// M = max_p m_p, w_p = 2^(m_p - M), O = sum_p w_p O_p / sum_p w_p l_p,
+// lse = ln2 (M + log2 l + lse_off), the parts taken in key order (m in log2
+// units; the fp8 kernel's weights are in units of 1/448, lse_off = -log2 448).
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int rid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -666,7 +667,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     *reinterpret_cast<uint32_t*>(static_cast<__bf16*>(a.o) + orow) = pack_bf16x2(o0 * inv, o1 * inv);
   }
   if (a.lse != nullptr && lane == 0)
-    a.lse[(int64_t)bh * a.N + row] = L > 0.f ? (M + __builtin_log2f(L)) * 0.69314718055994530942f : -INFINITY;
+    a.lse[(int64_t)bh * a.N + row] = L > 0.f ? (M + __builtin_log2f(L) + a.lse_off) * 0.69314718055994530942f
+                                           : -INFINITY;
 }
 
 }  // namespace

@@ -334,10 +334,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  // Work-group -> query block; a tail work-group also gets one of the
+  // `split` key-tile ranges [t0, t1) of its block.
+  int tile, part = -1;
+  if ((int)blockIdx.x < a.nfull) {
+    tile = xcd_remap(blockIdx.x, a.nfull);
+  } else {
+    const int j = blockIdx.x - a.nfull;
+    tile = a.nfull + j / a.split;
+    part = j % a.split;
+  }
   const int bh = tile / nqb, qblk = tile % nqb;
   const int b = bh / a.H, hd = bh % a.H;
   const int N = a.N, np = a.np, nb = a.nb;
+  const int t0 = part < 0 ? 0 : part * nb / a.split;
+  const int t1 = part < 0 ? nb : (part + 1) * nb / a.split;
 
   const uint8_t* q8 = a.q8 + (int64_t)bh * np * D;
   const uint8_t* k8 = a.k8 + (int64_t)bh * np * D;
@@ -371,27 +382,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
   }
   float m_run = -INFINITY, sv_prev = 1.f;
 
-  // ---- prologue: tiles 0 and 1 into LDS, tile 2 into registers ----
+  // ---- prologue: tiles t0 and t0+1 into LDS, t0+2 into registers ----
   Loader8<NT> ld;
-  ld.load(rk, rv, 0, np, tid);
+  ld.load(rk, rv, t0, np, tid);
   ld.store(smK[0], smV[0], tid);
-  ld.load(rk, rv, min(1, nb - 1), np, tid);
+  ld.load(rk, rv, min(t0 + 1, t1 - 1), np, tid);
   ld.store(smK[1], smV[1], tid);
-  ld.load(rk, rv, min(2, nb - 1), np, tid);
+  ld.load(rk, rv, min(t0 + 2, t1 - 1), np, tid);
   __syncthreads();
 
   f32x16 sacc[4];
   uint32_t p8[2][8];
   qk8_tile(sacc, smK[0], qf, l32, h);
-  softmax8(sacc, oacc, lacc, p8, m_run, sv_prev, fq * skp[0], svp[0], a.p_off, 0, N, h);
+  softmax8(sacc, oacc, lacc, p8, m_run, sv_prev, fq * skp[t0], svp[t0], a.p_off, t0 * BN8, N, h);
 
   int bc = 0;   // LDS buffer of tile t; tile t+1 is in bc+1, tile t+2 goes to bc+2 (mod 3)
-  for (int t = 0; t + 1 < nb; ++t) {
+  for (int t = t0; t + 1 < t1; ++t) {
     const int bn = (bc + 1 == NB8) ? 0 : bc + 1;
     const int bn2 = (bn + 1 == NB8) ? 0 : bn + 1;
     // Past the last tile the staged buffer is free and never read, and the
     // load repeats the last tile.
-    const int tload = min(t + 3, nb - 1);
+    const int tload = min(t + 3, t1 - 1);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -414,6 +425,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
   const float lt = lacc[0];
   const float inv = lt > 0.f ? sv_prev / lt : 0.f;
   const int row = q0 + l32;
+  if (part >= 0) {
+    // Partial result of one key range: A * sV_last (unnormalised O), m, l.
+    float* pr = a.part + ((int64_t)(blockIdx.x - a.nfull) * BM + wave * 32 + l32) * kPartRow;
+    if (row < N) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 t4 = {oacc[db][4 * r4 + 0] * sv_prev, oacc[db][4 * r4 + 1] * sv_prev,
+                            oacc[db][4 * r4 + 2] * sv_prev, oacc[db][4 * r4 + 3] * sv_prev};
+          *reinterpret_cast<f32x4*>(pr + db * 32 + r4 * 8 + h * 4) = t4;
+        }
+      if (h == 0) {
+        pr[128] = m_run;
+        pr[129] = lt;
+      }
+    }
+    return;
+  }
   if (row < N) {
     const int64_t orow = ob + (int64_t)row * a.os[2];
 #pragma unroll
@@ -446,13 +476,39 @@ hipError_t launch_fp8_quantize(const Fp8Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fp8(const Fp8Args& a, bool out_f32, hipStream_t s) {
+hipError_t launch_attn_fp8(const Fp8Args& args, bool out_f32, hipStream_t s) {
+  Fp8Args a = args;
   const int nqb = (a.N + 255) / 256;   // 8 waves x 32 query rows per work-group
-  const int64_t nwg = (int64_t)a.B * a.H * nqb;
+  int64_t nwg = (int64_t)a.B * a.H * nqb;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const bool split = a.split > 1 && a.part != nullptr;
+  if (split) {
+    if (a.nfull + a.ntail != nwg) return hipErrorInvalidConfiguration;
+    nwg = (int64_t)a.nfull + (int64_t)a.ntail * a.split;
+  } else {
+    a.nfull = (int)nwg;
+    a.ntail = 0;
+    a.split = 1;
+  }
   if (out_f32) hipLaunchKernelGGL((attn_fp8_kernel<8, true>), dim3((unsigned)nwg), dim3(512), 0, s, a, nqb);
   else hipLaunchKernelGGL((attn_fp8_kernel<8, false>), dim3((unsigned)nwg), dim3(512), 0, s, a, nqb);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  // Merge the split key ranges (the weights are in units of 1/448).
+  AttnArgs m = {};
+  m.o = a.o;
+  m.lse = a.lse;
+  for (int i = 0; i < 3; ++i) m.os[i] = a.os[i];
+  m.B = a.B;
+  m.H = a.H;
+  m.N = a.N;
+  m.nqb = nqb;
+  m.nfull = a.nfull;
+  m.ntail = a.ntail;
+  m.split = a.split;
+  m.part = a.part;
+  m.lse_off = -8.8073549220576041f;   // -log2(448)
+  return launch_attn_merge(m, out_f32, s);
 }
 
 }  // namespace dit

@@ -130,13 +130,13 @@ struct TailPlan {
   size_t bytes = 0;
 };
 
-TailPlan tail_plan(const dit_attn_shape* sh, int cus) {
+TailPlan tail_plan(const dit_attn_shape* sh, int cus, int tile_keys) {
   TailPlan t;
   const int64_t units = (int64_t)sh->batch * sh->heads * ((sh->seqlen + 255) / 256);
   t.nfull = (int)units;
   if (cus <= 0 || units > 0x7fffffff) return t;
   const int64_t full_rounds = units / cus, r = units % cus;
-  const int64_t tiles = (sh->seqlen + 63) / 64;
+  const int64_t tiles = (sh->seqlen + tile_keys - 1) / tile_keys;
   if (full_rounds < 1 || r == 0) return t;
   const int64_t split = std::min<int64_t>(cus / r, tiles);
   if (split < 2) return t;
@@ -148,14 +148,18 @@ TailPlan tail_plan(const dit_attn_shape* sh, int cus) {
 }
 
 struct Fp8Layout {
-  size_t q8, k8, v8t, sq, sk, sv, total;
+  size_t q8, k8, v8t, sq, sk, sv, part, total;
+  TailPlan plan;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Fp8Layout fp8_layout(int64_t BH, int64_t N) {
+// `sh` (may be null: no tail split) sizes the partial-result region of the
+// attention grid's tail split (128-key tiles) on the current device.
+Fp8Layout fp8_layout(int64_t BH, int64_t N, const dit_attn_shape* sh) {
   const int64_t nb = (N + 127) / 128, np = nb * 128;
   Fp8Layout L;
+  if (sh != nullptr) L.plan = tail_plan(sh, device_cus(), 128);
   const size_t codes = (size_t)(BH * np * 128), scales = (size_t)(BH * nb) * 4;
   L.q8 = 0;
   L.k8 = round256(L.q8 + codes);
@@ -163,7 +167,8 @@ Fp8Layout fp8_layout(int64_t BH, int64_t N) {
   L.sq = round256(L.v8t + codes);
   L.sk = round256(L.sq + scales);
   L.sv = round256(L.sk + scales);
-  L.total = round256(L.sv + scales);
+  L.part = round256(L.sv + scales);
+  L.total = round256(L.part + L.plan.bytes);
   return L;
 }
 
@@ -181,7 +186,7 @@ int prepare_fp8(const dit_attn_shape* sh, const void* q, const void* k, const vo
     if ((rc = check_common(&tmp, q, k, v, q, nullptr))) return rc;
   }
   const int64_t BH = (int64_t)sh->batch * sh->heads, N = sh->seqlen;
-  const Fp8Layout L = fp8_layout(BH, N);
+  const Fp8Layout L = fp8_layout(BH, N, sh);
   if (ws == nullptr) return fail(DIT_ATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
   if (!aligned(ws, 256)) return fail(DIT_ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   if (ws_bytes < L.total)
@@ -215,6 +220,10 @@ int prepare_fp8(const dit_attn_shape* sh, const void* q, const void* k, const vo
   f.sq = reinterpret_cast<float*>(base + L.sq);
   f.sk = reinterpret_cast<float*>(base + L.sk);
   f.sv = reinterpret_cast<float*>(base + L.sv);
+  f.nfull = L.plan.nfull;
+  f.ntail = L.plan.ntail;
+  f.split = L.plan.split;
+  f.part = L.plan.split > 1 ? reinterpret_cast<float*>(base + L.part) : nullptr;
   f.c = (float)((double)sh->softmax_scale * 1.4426950408889634);
   // 448 w = 2^(x + p_off) with p_off just below log2(448): the margin of
   // 2^-14 covers the rounding of the running max, so the product never
@@ -243,7 +252,7 @@ int dit_attn_fwd(const dit_attn_shape* shape, const void* q, const void* k, cons
 
 size_t dit_attn_fwd_workspace_bytes(const dit_attn_shape* shape) {
   if (shape == nullptr || shape->batch < 1 || shape->heads < 1 || shape->seqlen < 1) return 0;
-  return tail_plan(shape, device_cus()).bytes;
+  return tail_plan(shape, device_cus(), 64).bytes;
 }
 
 int dit_attn_fwd_ws(const dit_attn_shape* shape, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -251,7 +260,7 @@ int dit_attn_fwd_ws(const dit_attn_shape* shape, const void* q, const void* k, c
   g_err[0] = '\0';
   int rc = check_common(shape, q, k, v, o, lse);
   if (rc) return rc;
-  const TailPlan t = tail_plan(shape, device_cus());
+  const TailPlan t = tail_plan(shape, device_cus(), 64);
   dit::AttnArgs a;
   fill_common(shape, q, k, v, o, lse, a);
   if (t.split > 1) {
@@ -289,7 +298,7 @@ int dit_attn_fwd_blocksparse(const dit_attn_shape* shape, const void* q, const v
 
 size_t dit_attn_fwd_fp8_workspace_bytes(const dit_attn_shape* shape) {
   if (shape == nullptr || shape->batch < 1 || shape->heads < 1 || shape->seqlen < 1) return 0;
-  return fp8_layout((int64_t)shape->batch * shape->heads, shape->seqlen).total;
+  return fp8_layout((int64_t)shape->batch * shape->heads, shape->seqlen, shape).total;
 }
 
 int dit_attn_fp8_quantize(const dit_attn_shape* shape, const void* q, const void* k, const void* v,

@@ -27,6 +27,7 @@ struct AttnArgs {
   // combined by the merge kernel.  split == 1: no tail split.
   int nfull, ntail, split;
   float* part;          // [ntail * split][256 rows][kPartRow] fp32
+  float lse_off;        // added to log2 of the merged weight sum (0; fp8: -log2 448)
 };
 
 // fp32 words per row of a partial result: 128 unnormalised O, the row's
@@ -51,6 +52,9 @@ struct Fp8Args {
   float* sv;
   float c;              // softmax_scale * log2(e)
   float p_off;          // just below log2(448): w * 448 = exp2(x + p_off) <= 448
+  // Tail split of the attention grid, as for AttnArgs (split == 1: none).
+  int nfull, ntail, split;
+  float* part;          // [ntail * split][256 rows][kPartRow] fp32
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool out_f32, bool sparse, hipStream_t s);
