@@ -280,12 +280,18 @@ __device__ __forceinline__ void softmax8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f
                                          float& m_run, float& sv_prev, float f, float svt, float p_off, int key0,
                                          int N, int h) {
   if (key0 + BN8 > N) {
+    // Keys past N get -inf.  Element (kb, r) of this lane is key key0 + off
+    // + 4h with off = 32 kb + 8 (r/4) + r%4; each select uses its compare at
+    // once (the schedule barriers keep 64 compare masks from being live
+    // together in scalar registers).
+    const int rem = N - key0 - 4 * h;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        if (key >= N) sacc[kb][r] = -INFINITY;
+        const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+        sacc[kb][r] = off < rem ? sacc[kb][r] : -INFINITY;
+        __builtin_amdgcn_sched_barrier(0);
       }
   }
   const float vratio = sv_prev / svt;
