@@ -41,8 +41,12 @@ __device__ __forceinline__ int v8_pos_group(int kg) {
   return 8 * (kg & 1) + 4 * (kg >> 3) + ((kg >> 1) & 3);
 }
 
+// Four floats -> four e4m3 codes (a in the low byte).  The first convert
+// writes the low 16 bits and keeps the high half of its third operand, which
+// the second convert then overwrites, so any register serves as that
+// operand: a's own (dead after it), so no zeroed register or copy is needed.
 __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
