@@ -35,6 +35,14 @@
 //
 // The block-sparse variant runs the same per-tile arithmetic over the active
 // 128-key blocks of its query block only (masked blocks are never loaded).
+//
+// Tail split (dense, with a caller workspace): one 256-row work-group runs
+// per compute unit at a time, so the query blocks of a last, partial round
+// would leave most units idle.  Each of those blocks is instead split into
+// `split` consecutive key ranges run by separate work-groups (launched after
+// the full blocks); each range stores its unnormalised O, reference m c and
+// weight sum l, and attn_merge_kernel combines them in key order with the
+// exact rescaling 2^(m_p c - max m c).
 #include <type_traits>
 
 #include "device_common.h"
