@@ -34,7 +34,9 @@
 // optionally lse = ln2 * (m c + log2 l).
 //
 // The block-sparse variant runs the same per-tile arithmetic over the active
-// 128-key blocks of its query block only (masked blocks are never loaded).
+// 128-key blocks of its query block only (masked blocks are never loaded),
+// with two LDS buffers and its global loads issued two steps ahead in two
+// alternating register sets.
 //
 // Tail split (dense, with a caller workspace): one 256-row work-group runs
 // per compute unit at a time, so the query blocks of a last, partial round
@@ -555,26 +557,34 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     }
   } else {
-    // ---- prologue: tile 0 into LDS, tile 1 into registers ----
-    int k1 = -1;
+    // ---- prologue: tile 0 into LDS, tiles 1 and 2 into two register sets ----
+    // The kept blocks of a mask are scattered, so their loads miss L2 far more
+    // often than the dense walk's; each tile's loads are issued two steps
+    // before its LDS store, alternating between the two register sets.
+    TileLoader<NT> ld2;
+    int k1 = -1, k2 = -1;
     if (k0 >= 0) {
       ld.load(rk, rv, krow, vrow, k0, tid);
       ld.store(smK[0], smV[0], tid);
       k1 = tiles.next();
       ld.load(rk, rv, krow, vrow, k1 >= 0 ? k1 : N, tid);
+      k2 = k1 >= 0 ? tiles.next() : -1;
+      ld2.load(rk, rv, krow, vrow, k2 >= 0 ? k2 : N, tid);
     }
     __syncthreads();
 
     f32x16 sacc[2];
     uint32_t pk[2][8];
-    int kc = k0, kn = k1, bc = 0;
+    int kc = k0, kn = k1, kn2 = k2, bc = 0;
     bool first = true;   // wave-uniform
-    while (kc >= 0 && kc + BN <= N) {
-      // The staged tile goes to the other buffer even when there is none
-      // (that buffer is free), and loads past the last tile fetch key offset
-      // N, which the buffer bounds turn into zeros.
-      const int kn2 = kn >= 0 ? tiles.next() : -1;
-      const StepLoads<NT> sl = {ld, smK[bc ^ 1], smV[bc ^ 1], rk, rv, krow, vrow, kn2 >= 0 ? kn2 : N, tid};
+    // One full tile: L holds tile kn, which goes to the other buffer, and L
+    // then fetches the tile after kn2. The staged tile goes to the other
+    // buffer even when there is none (that buffer is free), and loads past
+    // the last tile fetch key offset N, which the buffer bounds turn into
+    // zeros.
+    auto full_step = [&](TileLoader<NT>& L) {
+      const int kn3 = kn2 >= 0 ? tiles.next() : -1;
+      const StepLoads<NT> sl = {L, smK[bc ^ 1], smV[bc ^ 1], rk, rv, krow, vrow, kn3 >= 0 ? kn3 : N, tid};
       mfma_range<0, 16, false, NT>(sacc, oacc, qf, pk, smK[bc], smV[bc], l32, h, lane, sl);
       softmax_next(sacc, st, oacc, pk, c, first);
       first = false;
@@ -582,7 +592,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
       __syncthreads();
       kc = kn;
       kn = kn2;
+      kn2 = kn3;
       bc ^= 1;
+    };
+    while (kc >= 0 && kc + BN <= N) {
+      full_step(ld);
+      if (!(kc >= 0 && kc + BN <= N)) break;
+      full_step(ld2);
     }
     if (kc >= 0) {   // ragged last tile
       qk_tile(sacc, smK[bc], qf, l32, h);
