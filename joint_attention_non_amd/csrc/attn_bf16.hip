@@ -187,21 +187,13 @@ __device__ __forceinline__ void qk_tile(f32x16 (&sacc)[2], const __bf16* sK, con
     }
 }
 
-// Keep a value computed at this point of the instruction stream: an empty
-// asm that reads and writes the register stops IR passes from sinking the
-// computation past the interleave points below (sched_barrier only binds
-// the machine scheduler).
-__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
-
 struct RowState {
   float m;    // running max of the raw dot products P is taken against
   float mc;   // m * c (0 until the first tile sets it)
   float l;    // this lane's partial sum of the rounded P
 };
 
-// Row max / sum over both lane halves of one query row (lanes l and l^32).
-__device__ __forceinline__ float row_max_halves(float x) { return fmaxf(x, swap_halves(x)); }
+// Sum over both lane halves of one query row (lanes l and l^32).
 __device__ __forceinline__ float row_sum_halves(float x) { return x + swap_halves(x); }
 
 // Move the running max when some row of the wave grew past the lazy bound
@@ -232,17 +224,6 @@ __device__ __forceinline__ float tile_max(const f32x16 (&sacc)[2]) {
     for (int r = 1; r < 8; ++r) t[j] = fmaxf(t[j], sacc[j >> 1][8 * (j & 1) + r]);
   }
   return max_halves(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
-}
-
-// Elements 2i and 2i+1 of the tile: P = 2^(S c - m c), rounded to a bf16
-// pair, and its rounded sum added to ls.
-__device__ __forceinline__ void exp_pair(const f32x16 (&sacc)[2], int i, float mc, float c,
-                                         uint32_t (&pk)[2][8], float& ls) {
-  const int kb = i >> 3, r = 2 * (i & 7);
-  const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][r], c, -mc));
-  const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][r + 1], c, -mc));
-  pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-  ls = sum_bf16x2(pk[kb][r >> 1], ls);
 }
 
 // P = 2^(S c - mc) for the 32 elements, rounded to bf16 pairs in pk; returns
