@@ -140,3 +140,17 @@ def test_fwd_ws_rejects_bad_shapes_before_any_device_call(mutate, status):
     bad = _shape()
     bad.seqlen = 0
     assert lib.dit_attn_fwd_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback path: without the built library every call raises."""
+    import torch
+    monkeypatch.setattr(dit, "_lib", None)
+    monkeypatch.setattr(dit, "_LIB_PATH", str(tmp_path / "libdit_attn.so"))
+    with pytest.raises(RuntimeError, match="is missing"):
+        dit.load()
+
+    # and host tensors are refused rather than computed on the CPU
+    q = torch.zeros((1, 1, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        dit.attn_fwd(q, q, q)
