@@ -185,3 +185,32 @@ def test_img2048_fp8_split_rows():
     assert torch.equal(o32.to(torch.bfloat16).view(torch.int16), o16a.view(torch.int16))
     _, ref_lse = oracle.attn(q, k, v, w.scale, rows=rows)
     assert np.max(np.abs(to64(lse.reshape(-1)[rows.to(DEV)].cpu()) - ref_lse)) <= 0.1
+
+
+def test_long_sequence_fp8_sampled():
+    """One head of 2^19 + 77 tokens: 4097 key blocks with a ragged last one,
+    and the last 256-row query block split over many key ranges (a single
+    partial round block on any device with more than one CU).  Rows outside
+    the split block are gated against the recipe, rows inside it as in the
+    split-row test."""
+    N = (1 << 19) + 77
+    _say(f"case: long sequence fp8 B1 H1 N{N}")
+    q, k, v = make_qkv(1, 1, N, 128, seed=63)
+    split_rows, split = _split_rows(1, 1, N)
+    first_split = int(split_rows[0]) if split_rows.numel() else N
+    g = torch.Generator().manual_seed(64)
+    plain = torch.unique(torch.cat([torch.tensor([0, 127, 128, N // 2, first_split - 1]),
+                                    torch.randint(0, first_split, (19,), generator=g)]))
+    e_rec, e_ref, e_rr = _fp8_vs_oracles(q, k, v, rows=plain)
+    _say(f"plain rows: vs recipe {e_rec}  vs exact {e_ref}  recipe vs exact {e_rr}")
+    assert e_rec["rel_l2"] <= FP8_RECIPE_REL_L2, e_rec
+    assert e_ref["cos"] >= FP8_COS, e_ref
+    if split_rows.numel():
+        _say(f"split rows={split_rows.numel()} parts={split}")
+        rows = torch.unique(torch.cat([split_rows[:2], split_rows[-2:],
+                                       split_rows[torch.randperm(split_rows.numel(), generator=g)[:12]]]))
+        e_rec, e_ref, e_rr = _fp8_vs_oracles(q, k, v, rows=rows)
+        _say(f"split rows: vs recipe {e_rec}  vs exact {e_ref}  recipe vs exact {e_rr}")
+        assert e_ref["cos"] >= FP8_COS, e_ref
+        assert e_ref["rel_l2"] <= e_rr["rel_l2"] * 1.05 + 1e-3, (e_ref, e_rr)
+        assert e_rec["rel_l2"] <= 0.05, e_rec
