@@ -27,7 +27,7 @@
 //                    the accumulator hands P out.  l accumulates the same
 //                    rounded P (v_dot2 with (1, 1)).
 // Software pipeline: step t issues the QK^T MFMAs of tile t+1 and the PV
-// MFMAs of tile t as one stream with their LDS operands read four MFMAs
+// MFMAs of tile t as one stream with their LDS operands read six MFMAs
 // ahead; the LDS stores of tile t+2 and the global loads of tile t+3 ride
 // on the PV MFMAs; then one barrier, then the softmax of tile t+1.
 // Epilogue: O = O^T / l, stored bf16 (round to nearest even) or fp32, and
@@ -291,12 +291,18 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[4], const uint32_t (&pk)[
 // One MFMA phase of the pipeline: S^T of the next tile (16 MFMAs, A = K
 // rows from sK) followed by O^T += V^T P^T of the current tile (16 MFMAs,
 // A = V^T from sV).  The 32 A operands are read from LDS as one stream kept
-// kPrefetch MFMAs ahead of their use, and the scheduler is told to keep that
-// interleave, so the LDS latency is covered by the matrix core's own work.
-// Riding on the PV half: the four 16-byte chunks of the staged tile are
-// stored to LDS (buffers sKs / sVs) and each register is refilled at once
+// prefetch_depth MFMAs ahead of their use, and the scheduler is told to keep
+// that interleave, so the LDS latency is covered by the matrix core's own
+// work.  Riding on the PV half: the four 16-byte chunks of the staged tile
+// are stored to LDS (buffers sKs / sVs) and each register is refilled at once
 // with the global load of the tile after it (key offset kload).
-constexpr int kPrefetch = 4;
+//
+// Depth 6 for the dense pipeline (8 waves) and 4 for the block-sparse one,
+// whose second load register set leaves no room for more: each measured
+// best for its kernel (4 -> 6 is about 0.8 % faster dense, 0.5 % slower
+// sparse).
+template <int NT>
+constexpr int prefetch_depth() { return NT == 512 ? 6 : 4; }
 
 template <int I>
 __device__ __forceinline__ bf16x8 step_operand(const __bf16* sK, const __bf16* sV, int l32, int h, int lane) {
@@ -325,17 +331,18 @@ struct StepLoads {
 template <int I, int FIRST, int LAST, bool LOADS, int NT>
 __device__ __forceinline__ void step_body(f32x16 (&sacc)[2], f32x16 (&oacc)[4], const bf16x8 (&qf)[8],
                                           const uint32_t (&pk)[2][8], const __bf16* sK, const __bf16* sV,
-                                          int l32, int h, int lane, bf16x8 (&fr)[kPrefetch + 1],
+                                          int l32, int h, int lane, bf16x8 (&fr)[prefetch_depth<NT>() + 1],
                                           const StepLoads<NT>& sl) {
+  constexpr int PF = prefetch_depth<NT>();
   if constexpr (I < LAST) {
-    if constexpr (I + kPrefetch < LAST)
-      fr[(I + kPrefetch) % (kPrefetch + 1)] = step_operand<I + kPrefetch>(sK, sV, l32, h, lane);
+    if constexpr (I + PF < LAST)
+      fr[(I + PF) % (PF + 1)] = step_operand<I + PF>(sK, sV, l32, h, lane);
     if constexpr (I < 16) {
       constexpr int s = I >> 1, kb = I & 1;
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[I % (kPrefetch + 1)], qf[s], sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[I % (PF + 1)], qf[s], sacc[kb], 0, 0, 0);
     } else {
       constexpr int j = I - 16, s4 = j >> 2, db = j & 3;
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[I % (kPrefetch + 1)], p_operand(pk, s4),
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[I % (PF + 1)], p_operand(pk, s4),
                                                          oacc[db], 0, 0, 0);
       if constexpr (LOADS) {
         constexpr int CH = TileLoader<NT>::CH, every = 16 / CH;
@@ -349,17 +356,27 @@ __device__ __forceinline__ void step_body(f32x16 (&sacc)[2], f32x16 (&oacc)[4], 
   }
 }
 
-template <int I, int LAST, bool LOADS, int CH>
+template <int I, int LAST, bool LOADS, int CH, int PF>
 __device__ __forceinline__ void step_schedule() {
   if constexpr (I < LAST) {
-    if constexpr (I + kPrefetch < LAST)
-      __builtin_amdgcn_sched_group_barrier(0x100, I + kPrefetch < 16 ? 1 : 2, 0);   // LDS reads
+    if constexpr (I + PF < LAST)
+      __builtin_amdgcn_sched_group_barrier(0x100, I + PF < 16 ? 1 : 2, 0);          // LDS reads
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             // one MFMA
     if constexpr (LOADS && I >= 16 && ((I - 16) % (16 / CH)) == 0) {
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                           // LDS store
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                           // global load
     }
-    step_schedule<I + 1, LAST, LOADS, CH>();
+    step_schedule<I + 1, LAST, LOADS, CH, PF>();
+  }
+}
+
+// Operand reads of MFMAs [I, END) before the first MFMA of a range.
+template <int I, int END, int PF>
+__device__ __forceinline__ void prefetch_operands(bf16x8 (&fr)[PF + 1], const __bf16* sK, const __bf16* sV,
+                                                  int l32, int h, int lane) {
+  if constexpr (I < END) {
+    fr[I % (PF + 1)] = step_operand<I>(sK, sV, l32, h, lane);
+    prefetch_operands<I + 1, END, PF>(fr, sK, sV, l32, h, lane);
   }
 }
 
@@ -367,7 +384,8 @@ template <int FIRST, int LAST, bool LOADS, int NT>
 __device__ __forceinline__ void mfma_range(f32x16 (&sacc)[2], f32x16 (&oacc)[4], const bf16x8 (&qf)[8],
                                            const uint32_t (&pk)[2][8], const __bf16* sK, const __bf16* sV,
                                            int l32, int h, int lane, const StepLoads<NT>& sl) {
-  static_assert(LAST - FIRST >= kPrefetch && kPrefetch == 4, "prologue reads");
+  constexpr int PF = prefetch_depth<NT>();
+  static_assert(LAST - FIRST >= PF && (FIRST >= 16 || FIRST + PF <= 16), "prologue reads in one half");
   static_assert(16 % TileLoader<NT>::CH == 0, "staged chunks spread over the PV MFMAs");
   if constexpr (FIRST == 0) {
 #pragma unroll
@@ -375,14 +393,11 @@ __device__ __forceinline__ void mfma_range(f32x16 (&sacc)[2], f32x16 (&oacc)[4],
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
   }
-  bf16x8 fr[kPrefetch + 1];
-  fr[FIRST % (kPrefetch + 1)] = step_operand<FIRST>(sK, sV, l32, h, lane);
-  fr[(FIRST + 1) % (kPrefetch + 1)] = step_operand<FIRST + 1>(sK, sV, l32, h, lane);
-  fr[(FIRST + 2) % (kPrefetch + 1)] = step_operand<FIRST + 2>(sK, sV, l32, h, lane);
-  fr[(FIRST + 3) % (kPrefetch + 1)] = step_operand<FIRST + 3>(sK, sV, l32, h, lane);
+  bf16x8 fr[PF + 1];
+  prefetch_operands<FIRST, FIRST + PF, PF>(fr, sK, sV, l32, h, lane);
   step_body<FIRST, FIRST, LAST, LOADS, NT>(sacc, oacc, qf, pk, sK, sV, l32, h, lane, fr, sl);
-  __builtin_amdgcn_sched_group_barrier(0x100, (FIRST < 16 ? 1 : 2) * kPrefetch, 0);
-  step_schedule<FIRST, LAST, LOADS, TileLoader<NT>::CH>();
+  __builtin_amdgcn_sched_group_barrier(0x100, (FIRST < 16 ? 1 : 2) * PF, 0);
+  step_schedule<FIRST, LAST, LOADS, TileLoader<NT>::CH, PF>();
 }
 
 // One MFMA phase of the dense pipeline: QK^T of the next tile and PV of the

@@ -163,6 +163,16 @@ __device__ __forceinline__ i32x8 op8(const uint8_t* sK, const uint8_t* sV, int l
   else return lds_frag8(sV + (((J - 8) & 3) * 32 + l32) * RS8 + 64 * ((J - 8) >> 2) + 32 * h);
 }
 
+// Operands [I, kPre8) of a step, read before its first MFMA.
+template <int I>
+__device__ __forceinline__ void prefetch8(i32x8 (&fr)[kPre8 + 1], const uint8_t* sK, const uint8_t* sV, int l32,
+                                          int h) {
+  if constexpr (I < kPre8) {
+    fr[I] = op8<I>(sK, sV, l32, h);
+    prefetch8<I + 1>(fr, sK, sV, l32, h);
+  }
+}
+
 __device__ __forceinline__ i32x8 p_frag8(const uint32_t (&p8)[2][8], int s) {
   return i32x8{(int)p8[s][0], (int)p8[s][1], (int)p8[s][2], (int)p8[s][3],
                (int)p8[s][4], (int)p8[s][5], (int)p8[s][6], (int)p8[s][7]};
@@ -418,8 +428,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
     i32x8 fr[kPre8 + 1];
-    fr[0] = op8<0>(smK[bn], smV[bc], l32, h);
-    fr[1] = op8<1>(smK[bn], smV[bc], l32, h);
+    prefetch8<0>(fr, smK[bn], smV[bc], l32, h);
     step8<0, NT>(sacc, oacc, lacc, qf, p8, smK[bn], smV[bc], l32, h, fr, ld, smK[bn2], smV[bn2], rk, rv, tload,
                  np, tid);
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre8, 0);
