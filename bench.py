@@ -192,7 +192,7 @@ def main():
     log(f"[bench] {w.name}: per-launch {stats}")
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "attn_bf16_kernel<8,3,false,false>",
+                "traffic": traffic, "kernel": "attn_dense_kernel<false>",
                 "flops_per_launch": flops}
     log(f"[bench] {w.name}: {ms:.3f} ms  {tflops:.1f} TFLOP/s  {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak"
         f"  (without the tail split {ms_plain:.3f} ms)")

@@ -84,14 +84,14 @@ int dit_attn_fwd(const dit_attn_shape* shape,
 
 /* Workspace bytes dit_attn_fwd_ws needs for `shape` on the current device
  * (0: no split applies, the workspace may be NULL; also 0 for an invalid
- * shape).  Layout: fp32 [P][256][132], one row per query row of each of the
+ * shape).  Layout: fp32 [P][384][132], one row per query row of each of the
  * P = ntail * split tail work-groups: 128 unnormalised O values, m * scale
  * * log2(e), the row's weight sum, 2 words of padding. */
 size_t dit_attn_fwd_workspace_bytes(const dit_attn_shape* shape);
 
 /* The same attention as dit_attn_fwd (same operation, same arguments and
  * errors), with a caller workspace for load balancing: the query blocks of
- * 256 rows run one per compute unit, and those of the last, partial round
+ * 384 rows run one per compute unit, and those of the last, partial round
  * are each split into key ranges whose partial results (own running max,
  * unnormalised O and weight sum) are combined by a second kernel in key
  * order: O = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p with M = max m_p.
@@ -156,8 +156,10 @@ int dit_attn_fp8_quantize(const dit_attn_shape* shape,
  * = attend.  Masked blocks act as -inf logits: they are skipped and their K
  * and V are never read.  mask_stride_bh is the element offset between the
  * masks of consecutive (b, h) slices (b-major); 0 shares one mask.
- * block_size must be 128.  The arithmetic per kept block is identical to
- * dit_attn_fwd, so an all-ones mask reproduces it bit for bit. */
+ * block_size must be 128.  The per-tile arithmetic is that of dit_attn_fwd
+ * (fp32 scores, P rounded to bf16, row sums over the rounded P) in 64-key
+ * tiles on 128-row blocks, so an all-ones mask reproduces dit_attn_fwd
+ * within the same tolerance, not bit for bit. */
 int dit_attn_fwd_blocksparse(const dit_attn_shape* shape,
                              const void* q, const void* k, const void* v,
                              void* o, float* lse,

@@ -128,16 +128,6 @@ __device__ __forceinline__ bf16x8 v_operand(const __bf16* sV, int s4, int db, in
   return __builtin_bit_cast(bf16x8, v);
 }
 
-struct DenseTiles {
-  int pos, N;
-  __device__ __forceinline__ int next() {
-    if (pos >= N) return -1;
-    const int k = pos;
-    pos += BN;
-    return k;
-  }
-};
-
 // Active 128-key blocks of one mask row, found 64 at a time with a ballot;
 // every value here is wave-uniform.
 struct SparseTiles {
@@ -244,14 +234,6 @@ __device__ __forceinline__ float exp_tile_sum(const f32x16 (&sacc)[2], float mc,
   return (ls[0] + ls[1]) + (ls[2] + ls[3]);
 }
 
-// First tile of a row block: move the running max to the tile's max, then
-// take the exponentials against it.
-__device__ __forceinline__ void softmax_first(const f32x16 (&sacc)[2], RowState& st, f32x16 (&oacc)[4],
-                                              uint32_t (&pk)[2][8], float c) {
-  maybe_rescale(tile_max(sacc), st, oacc, c);
-  st.l += exp_tile_sum(sacc, st.mc, pk, c);
-}
-
 // Later tiles: take the exponentials against the current reference
 // straight away.  Weights far above 1 are harmless in floating point (the
 // row sum and O keep their relative precision), so the tile is kept unless a
@@ -297,12 +279,10 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[4], const uint32_t (&pk)[
 // are stored to LDS (buffers sKs / sVs) and each register is refilled at once
 // with the global load of the tile after it (key offset kload).
 //
-// Depth 6 for the dense pipeline (8 waves) and 4 for the block-sparse one,
-// whose second load register set leaves no room for more: each measured
-// best for its kernel (4 -> 6 is about 0.8 % faster dense, 0.5 % slower
-// sparse).
+// Depth 4: the kernel's second load register set leaves no room for more
+// (6 measured 0.5 % slower).
 template <int NT>
-constexpr int prefetch_depth() { return NT == 512 ? 6 : 4; }
+constexpr int prefetch_depth() { return 4; }
 
 template <int I>
 __device__ __forceinline__ bf16x8 step_operand(const __bf16* sK, const __bf16* sV, int l32, int h, int lane) {
@@ -400,15 +380,6 @@ __device__ __forceinline__ void mfma_range(f32x16 (&sacc)[2], f32x16 (&oacc)[4],
   step_schedule<FIRST, LAST, LOADS, TileLoader<NT>::CH, PF>();
 }
 
-// One MFMA phase of the dense pipeline: QK^T of the next tile and PV of the
-// current one, with the staging of the tile after next riding on the PV.
-template <int NT>
-__device__ __forceinline__ void mfma_step(f32x16 (&sacc)[2], f32x16 (&oacc)[4], const bf16x8 (&qf)[8],
-                                          const uint32_t (&pk)[2][8], const __bf16* sK, const __bf16* sV,
-                                          int l32, int h, int lane, const StepLoads<NT>& sl) {
-  mfma_range<0, 32, true, NT>(sacc, oacc, qf, pk, sK, sV, l32, h, lane, sl);
-}
-
 __device__ __forceinline__ void mask_tail(f32x16 (&sacc)[2], int key0, int N, int h) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -419,31 +390,21 @@ __device__ __forceinline__ void mask_tail(f32x16 (&sacc)[2], int key0, int N, in
     }
 }
 
-// NBUF = 3: three rotating tile buffers and the offset two-wave pipeline
-// below (8 waves, one work-group per CU).  NBUF = 2: double buffering with
-// one tile in flight and a plain per-tile loop (4 waves; two work-groups fit
-// a CU, which is what the block-sparse launch uses).  Per query row both
-// perform the same operations on the same tiles in the same order.
-template <int NW, int NBUF, bool OUT_F32, bool SPARSE>
-__global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
+// Block-sparse kernel: a work-group of 4 waves owns one 128-row mask block
+// (each wave 32 rows); two work-groups share a CU.  K and V of the kept key
+// blocks pass through two LDS buffers.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 2) void attn_sparse_kernel(AttnArgs a) {
+  constexpr int NW = 4;
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
-  static_assert(!SPARSE || BM == kBlock, "block-sparse work-groups cover one 128-row mask block");
-  __shared__ __attribute__((aligned(16))) __bf16 smK[NBUF][BN * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 smV[NBUF][BN * VSR];
+  static_assert(BM == kBlock, "block-sparse work-groups cover one 128-row mask block");
+  __shared__ __attribute__((aligned(16))) __bf16 smK[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) __bf16 smV[2][BN * VSR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  // Work-group -> query block; a tail work-group (dense only) also gets one
-  // of the `split` key ranges of its block.
-  int tile, part = -1;
-  if ((int)blockIdx.x < a.nfull) {
-    tile = xcd_remap(blockIdx.x, a.nfull);
-  } else {
-    const int j = blockIdx.x - a.nfull;
-    tile = a.nfull + j / a.split;
-    part = j % a.split;
-  }
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / a.nqb, qblk = tile % a.nqb;
   const int b = bh / a.H, hd = bh % a.H;
   const int N = a.N;
@@ -474,134 +435,64 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   RowState st = {-INFINITY, 0.f, 0.f};
 
-  typename std::conditional<SPARSE, SparseTiles, DenseTiles>::type tiles;
-  if constexpr (SPARSE) {
-    tiles.row = a.mask + (int64_t)bh * a.mask_bh + (int64_t)qblk * a.nb;
-    tiles.nb = a.nb;
-    tiles.N = N;
-    tiles.chunk = -1;
-    tiles.pend = -1;
-    tiles.bits = 0;
-  } else {
-    // Key tiles [t0, t1) of nt for part p of `split`: t = p * nt / split.
-    int kbeg = 0, kend = N;
-    if (part >= 0) {
-      const int nt = (N + BN - 1) / BN;
-      kbeg = part * nt / a.split * BN;
-      kend = min((part + 1) * nt / a.split * BN, N);
-    }
-    tiles.pos = kbeg;
-    tiles.N = kend;
-  }
+  SparseTiles tiles;
+  tiles.row = a.mask + (int64_t)bh * a.mask_bh + (int64_t)qblk * a.nb;
+  tiles.nb = a.nb;
+  tiles.N = N;
+  tiles.chunk = -1;
+  tiles.pend = -1;
+  tiles.bits = 0;
 
   TileLoader<NT> ld;
   const int k0 = tiles.next();
-  if constexpr (NBUF == 3) {
-    // ---- prologue: tiles 0 and 1 into LDS, tile 2 into registers ----
-    int k1 = -1, k2 = -1;
-    if (k0 >= 0) {
-      ld.load(rk, rv, krow, vrow, k0, tid);
-      ld.store(smK[0], smV[0], tid);
-      k1 = tiles.next();
-      if (k1 >= 0) {
-        ld.load(rk, rv, krow, vrow, k1, tid);
-        ld.store(smK[1], smV[1], tid);
-        k2 = tiles.next();
-      }
-      ld.load(rk, rv, krow, vrow, k2 >= 0 ? k2 : N, tid);
-    }
+  // ---- prologue: tile 0 into LDS, tiles 1 and 2 into two register sets ----
+  // The kept blocks of a mask are scattered, so their loads miss L2 far more
+  // often than the dense walk's; each tile's loads are issued two steps
+  // before its LDS store, alternating between the two register sets.
+  TileLoader<NT> ld2;
+  int k1 = -1, k2 = -1;
+  if (k0 >= 0) {
+    ld.load(rk, rv, krow, vrow, k0, tid);
+    ld.store(smK[0], smV[0], tid);
+    k1 = tiles.next();
+    ld.load(rk, rv, krow, vrow, k1 >= 0 ? k1 : N, tid);
+    k2 = k1 >= 0 ? tiles.next() : -1;
+    ld2.load(rk, rv, krow, vrow, k2 >= 0 ? k2 : N, tid);
+  }
+  __syncthreads();
+
+  f32x16 sacc[2];
+  uint32_t pk[2][8];
+  int kc = k0, kn = k1, kn2 = k2, bc = 0;
+  bool first = true;   // wave-uniform
+  // One full tile: L holds tile kn, which goes to the other buffer, and L
+  // then fetches the tile after kn2. The staged tile goes to the other
+  // buffer even when there is none (that buffer is free), and loads past
+  // the last tile fetch key offset N, which the buffer bounds turn into
+  // zeros.
+  auto full_step = [&](TileLoader<NT>& L) {
+    const int kn3 = kn2 >= 0 ? tiles.next() : -1;
+    const StepLoads<NT> sl = {L, smK[bc ^ 1], smV[bc ^ 1], rk, rv, krow, vrow, kn3 >= 0 ? kn3 : N, tid};
+    mfma_range<0, 16, false, NT>(sacc, oacc, qf, pk, smK[bc], smV[bc], l32, h, lane, sl);
+    softmax_next(sacc, st, oacc, pk, c, first);
+    first = false;
+    mfma_range<16, 32, true, NT>(sacc, oacc, qf, pk, smK[bc], smV[bc], l32, h, lane, sl);
     __syncthreads();
-
-    if (k0 >= 0) {
-      f32x16 sacc[2];
-      uint32_t pk[2][8];
-      qk_tile(sacc, smK[0], qf, l32, h);
-      if (k0 + BN > N) mask_tail(sacc, k0, N, h);
-      softmax_first(sacc, st, oacc, pk, c);
-      int kn = k1, kn2 = k2;
-      int bc = 0;   // LDS buffer of the current tile; kn sits in bc+1, kn2 goes to bc+2 (mod 3)
-
-      // ---- steady state: step t = [QK^T(t+1), PV(t)], barrier, [softmax(t+1)] ----
-      // The barrier right after the MFMA block publishes tile t+2 (stored
-      // during the PV MFMAs) and frees tile t's buffer; the softmax needs no
-      // LDS, so it runs after it.
-      while (kn >= 0 && kn + BN <= N) {
-        const int bn = (bc + 1 == NBUF) ? 0 : bc + 1;
-        const int bn2 = (bn + 1 == NBUF) ? 0 : bn + 1;
-        // The staged tile goes to buffer bn2 even past the last tile (that
-        // buffer is free; nothing reads it), and loads past the end fetch
-        // key offset N, which the buffer bounds turn into zeros.
-        const int kn3 = tiles.next();
-        const StepLoads<NT> sl = {ld, smK[bn2], smV[bn2], rk, rv, krow, vrow, kn3 >= 0 ? kn3 : N, tid};
-        mfma_step<NT>(sacc, oacc, qf, pk, smK[bn], smV[bc], l32, h, lane, sl);
-        __syncthreads();
-        softmax_next(sacc, st, oacc, pk, c);
-        kn = kn2;
-        kn2 = kn3;
-        bc = bn;
-      }
-
-      // ---- drain: PV of the current tile, then a ragged last tile if there
-      // is one (already in LDS; keys past N get -inf) ----
-      pv_tile(oacc, pk, smV[bc], lane);
-      if (kn >= 0) {
-        const int bn = (bc + 1 == NBUF) ? 0 : bc + 1;
-        qk_tile(sacc, smK[bn], qf, l32, h);
-        mask_tail(sacc, kn, N, h);
-        softmax_next(sacc, st, oacc, pk, c);
-        pv_tile(oacc, pk, smV[bn], lane);
-      }
-    }
-  } else {
-    // ---- prologue: tile 0 into LDS, tiles 1 and 2 into two register sets ----
-    // The kept blocks of a mask are scattered, so their loads miss L2 far more
-    // often than the dense walk's; each tile's loads are issued two steps
-    // before its LDS store, alternating between the two register sets.
-    TileLoader<NT> ld2;
-    int k1 = -1, k2 = -1;
-    if (k0 >= 0) {
-      ld.load(rk, rv, krow, vrow, k0, tid);
-      ld.store(smK[0], smV[0], tid);
-      k1 = tiles.next();
-      ld.load(rk, rv, krow, vrow, k1 >= 0 ? k1 : N, tid);
-      k2 = k1 >= 0 ? tiles.next() : -1;
-      ld2.load(rk, rv, krow, vrow, k2 >= 0 ? k2 : N, tid);
-    }
-    __syncthreads();
-
-    f32x16 sacc[2];
-    uint32_t pk[2][8];
-    int kc = k0, kn = k1, kn2 = k2, bc = 0;
-    bool first = true;   // wave-uniform
-    // One full tile: L holds tile kn, which goes to the other buffer, and L
-    // then fetches the tile after kn2. The staged tile goes to the other
-    // buffer even when there is none (that buffer is free), and loads past
-    // the last tile fetch key offset N, which the buffer bounds turn into
-    // zeros.
-    auto full_step = [&](TileLoader<NT>& L) {
-      const int kn3 = kn2 >= 0 ? tiles.next() : -1;
-      const StepLoads<NT> sl = {L, smK[bc ^ 1], smV[bc ^ 1], rk, rv, krow, vrow, kn3 >= 0 ? kn3 : N, tid};
-      mfma_range<0, 16, false, NT>(sacc, oacc, qf, pk, smK[bc], smV[bc], l32, h, lane, sl);
-      softmax_next(sacc, st, oacc, pk, c, first);
-      first = false;
-      mfma_range<16, 32, true, NT>(sacc, oacc, qf, pk, smK[bc], smV[bc], l32, h, lane, sl);
-      __syncthreads();
-      kc = kn;
-      kn = kn2;
-      kn2 = kn3;
-      bc ^= 1;
-    };
-    while (kc >= 0 && kc + BN <= N) {
-      full_step(ld);
-      if (!(kc >= 0 && kc + BN <= N)) break;
-      full_step(ld2);
-    }
-    if (kc >= 0) {   // ragged last tile
-      qk_tile(sacc, smK[bc], qf, l32, h);
-      mask_tail(sacc, kc, N, h);
-      softmax_next(sacc, st, oacc, pk, c, first);
-      pv_tile(oacc, pk, smV[bc], lane);
-    }
+    kc = kn;
+    kn = kn2;
+    kn2 = kn3;
+    bc ^= 1;
+  };
+  while (kc >= 0 && kc + BN <= N) {
+    full_step(ld);
+    if (!(kc >= 0 && kc + BN <= N)) break;
+    full_step(ld2);
+  }
+  if (kc >= 0) {   // ragged last tile
+    qk_tile(sacc, smK[bc], qf, l32, h);
+    mask_tail(sacc, kc, N, h);
+    softmax_next(sacc, st, oacc, pk, c, first);
+    pv_tile(oacc, pk, smV[bc], lane);
   }
 
   // ---- epilogue ----
@@ -609,26 +500,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   const float lt = row_sum_halves(st.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int row = q0 + l32;
-  if constexpr (!SPARSE) {
-    if (part >= 0) {
-      // Partial result of one key range: unnormalised O, m c and l.
-      float* pr = a.part + ((int64_t)(blockIdx.x - a.nfull) * BM + wave * 32 + l32) * kPartRow;
-      if (row < N) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 t = {oacc[db][4 * r4 + 0], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2], oacc[db][4 * r4 + 3]};
-            *reinterpret_cast<f32x4*>(pr + db * 32 + r4 * 8 + h * 4) = t;
-          }
-        if (h == 0) {
-          pr[128] = st.mc;
-          pr[129] = lt;
-        }
-      }
-      return;
-    }
-  }
   if (row < N) {
     const int64_t orow = ob + (int64_t)row * a.os[2];
 #pragma unroll
@@ -652,6 +523,376 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+// ---- dense kernel: 48 query rows per wave on the 16x16x32 MFMA ----
+
+constexpr int RBN = 32;                 // keys per tile
+constexpr int RNB = 3;                  // LDS tile buffers
+constexpr int RRB = 3;                  // 16-row blocks per wave
+constexpr int RNW = 8;                  // waves per work-group
+constexpr int RBM = RNW * 16 * RRB;     // 384 query rows per work-group
+static_assert(RBM == kDenseRows && RBN == kDenseTileKeys, "the host plans with these sizes");
+constexpr int RNT = RNW * 64;
+
+struct RLoader {
+  // 32 keys x 16 chunks of 16 bytes, for K (I = 0) and V (I = 1).
+  u32x4 r[2];
+  template <int I>
+  __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t krow,
+                                           uint32_t vrow, int key0, int N, int tid) {
+    const int key = tid >> 4, c = tid & 15;
+    const int row = min(key0 + key, N);
+    r[I] = buf_load_b128(I == 0 ? rk : rv, (uint32_t)row * (I == 0 ? krow : vrow) + c * 16);
+  }
+  template <int I>
+  __device__ __forceinline__ void store_one(__bf16* sk, __bf16* sv, int tid) const {
+    const int key = tid >> 4, c = tid & 15;
+    *reinterpret_cast<u32x4*>((I == 0 ? sk + key * KS : sv + key * VSR) + c * 8) = r[I];
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t krow,
+                                       uint32_t vrow, int key0, int N, int tid) {
+    load_one<0>(rk, rv, krow, vrow, key0, N, tid);
+    load_one<1>(rk, rv, krow, vrow, key0, N, tid);
+  }
+  __device__ __forceinline__ void store(__bf16* sk, __bf16* sv, int tid) const {
+    store_one<0>(sk, sv, tid);
+    store_one<1>(sk, sv, tid);
+  }
+};
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A operand J of a step: J < 8 -> K fragment (ds, kb) = (J / 2, J % 2):
+// rows 16 kb + l % 16, d 32 ds + 8 g .. +7.  J >= 8 -> V^T operand, d block
+// db = J - 8: lane (g, s) reads rows 4g + s/4 (+16), columns 16 db + 4 (s%4).
+__device__ __forceinline__ bf16x8 r_v_operand(const __bf16* sV, int db, int g, int s) {
+  const __bf16* base = sV + (4 * g + (s >> 2)) * VSR + 16 * db + 4 * (s & 3);
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base));
+  const s16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + 16 * VSR));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int J>
+__device__ __forceinline__ bf16x8 r_operand(const __bf16* sK, const __bf16* sV, int l16, int g, int s) {
+  if constexpr (J < 8) {
+    return *reinterpret_cast<const bf16x8*>(sK + ((J & 1) * 16 + l16) * KS + 32 * (J >> 1) + 8 * g);
+  } else {
+    return r_v_operand(sV, J - 8, g, s);
+  }
+}
+
+__device__ __forceinline__ bf16x8 r_p_operand(const uint32_t (&pk)[4]) {
+  const u32x4 t = {pk[0], pk[1], pk[2], pk[3]};
+  return __builtin_bit_cast(bf16x8, t);
+}
+
+constexpr int kRPre = 3;   // operand pairs read this many steps ahead (2-4 measured within 1 %)
+
+// Operand pair I of a step (0..15), three MFMAs each (row blocks).  With
+// staging, the K and V chunks of the staged tile are stored at I = 8 and 12
+// and the registers refilled with the tile after it.
+template <int I>
+__device__ __forceinline__ void r_step(f32x4 (&sacc)[2][RRB], f32x4 (&oacc)[8][RRB], const bf16x8 (&qf)[RRB][4],
+                                       const uint32_t (&pk)[RRB][4], const __bf16* sK, const __bf16* sV, int l16,
+                                       int g, int s, bf16x8 (&fr)[kRPre + 1], RLoader& ld, __bf16* sks, __bf16* svs,
+                                       __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t krow,
+                                       uint32_t vrow, int kload, int N, int tid) {
+  if constexpr (I < 16) {
+    if constexpr (I + kRPre < 16) fr[(I + kRPre) % (kRPre + 1)] = r_operand<I + kRPre>(sK, sV, l16, g, s);
+    const bf16x8 a = fr[I % (kRPre + 1)];
+    if constexpr (I < 8) {
+      constexpr int ds = I >> 1, kb = I & 1;
+#pragma unroll
+      for (int rb = 0; rb < RRB; ++rb) sacc[kb][rb] = mfma16(a, qf[rb][ds], sacc[kb][rb]);
+    } else {
+      constexpr int db = I - 8;
+#pragma unroll
+      for (int rb = 0; rb < RRB; ++rb) oacc[db][rb] = mfma16(a, r_p_operand(pk[rb]), oacc[db][rb]);
+      if constexpr (I == 8) {
+        ld.template store_one<0>(sks, svs, tid);
+        ld.template load_one<0>(rk, rv, krow, vrow, kload, N, tid);
+      }
+      if constexpr (I == 12) {
+        ld.template store_one<1>(sks, svs, tid);
+        ld.template load_one<1>(rk, rv, krow, vrow, kload, N, tid);
+      }
+    }
+    r_step<I + 1>(sacc, oacc, qf, pk, sK, sV, l16, g, s, fr, ld, sks, svs, rk, rv, krow, vrow, kload, N, tid);
+  }
+}
+
+template <int I>
+__device__ __forceinline__ void r_step_schedule() {
+  if constexpr (I < 16) {
+    if constexpr (I + kRPre < 16) __builtin_amdgcn_sched_group_barrier(0x100, I + kRPre < 8 ? 1 : 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, RRB, 0);
+    if constexpr (I == 8 || I == 12) {
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    r_step_schedule<I + 1>();
+  }
+}
+
+// Max over the 8 keys a lane holds of row block rb, then over the 4 lane
+// groups sharing the query row (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float r_row_max(const f32x4 (&sacc)[2][RRB], int rb) {
+  float m = fmaxf(fmaxf(fmaxf(sacc[0][rb][0], sacc[0][rb][1]), fmaxf(sacc[0][rb][2], sacc[0][rb][3])),
+                  fmaxf(fmaxf(sacc[1][rb][0], sacc[1][rb][1]), fmaxf(sacc[1][rb][2], sacc[1][rb][3])));
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  return max_halves(m);
+}
+__device__ __forceinline__ float r_row_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + swap_halves(x);
+}
+
+__device__ __forceinline__ void r_rescale(float t, RowState& st, f32x4 (&oacc)[8][RRB], int rb, float c) {
+  const bool grow = (t - st.m) * c > kLazy;
+  if (__any(grow)) {
+    const float mnew = fmaxf(st.m, t);
+    const float alpha = fast_exp2((st.m - mnew) * c);
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[db][rb][r] *= alpha;
+    st.m = mnew;
+    st.mc = mnew * c;
+  }
+}
+
+// P for row block rb: 2^(S c - mc) rounded to bf16 pairs in the B-operand
+// order (keys 4g..4g+3, then 16+4g..16+4g+3); returns the lane's sum of the
+// rounded P.
+__device__ __forceinline__ float r_exp_block(const f32x4 (&sacc)[2][RRB], int rb, float mc, float c,
+                                             uint32_t (&pk)[4]) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(sacc[i >> 2][rb][i & 3], c, -mc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = fast_exp2(x[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+  float ls0 = sum_bf16x2(pk[0], 0.f), ls1 = sum_bf16x2(pk[1], 0.f);
+  ls0 = sum_bf16x2(pk[2], ls0);
+  ls1 = sum_bf16x2(pk[3], ls1);
+  return ls0 + ls1;
+}
+
+__device__ __forceinline__ void r_mask(f32x4 (&sacc)[2][RRB], int key0, int N, int g) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + kb * 16 + 4 * g + r;
+      if (key >= N) {
+#pragma unroll
+        for (int rb = 0; rb < RRB; ++rb) sacc[kb][rb][r] = -INFINITY;
+      }
+    }
+}
+
+// Softmax of one tile for the three row blocks (first: take the tile max as
+// the reference first; later tiles keep the reference unless a lane's
+// weights pass 2^64).
+__device__ __forceinline__ void r_softmax(f32x4 (&sacc)[2][RRB], RowState (&st)[RRB], f32x4 (&oacc)[8][RRB],
+                                          uint32_t (&pk)[RRB][4], float c, bool first) {
+#pragma unroll
+  for (int rb = 0; rb < RRB; ++rb) {
+    float ls = 0.f;
+    if (!first) ls = r_exp_block(sacc, rb, st[rb].mc, c, pk[rb]);
+    if (first || __any(!(ls <= kCheck))) {
+      r_rescale(r_row_max(sacc, rb), st[rb], oacc, rb, c);
+      ls = r_exp_block(sacc, rb, st[rb].mc, c, pk[rb]);
+    }
+    st[rb].l += ls;
+  }
+}
+
+__device__ __forceinline__ void r_qk_tile(f32x4 (&sacc)[2][RRB], const __bf16* sK, const bf16x8 (&qf)[RRB][4],
+                                          int l16, int g) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int rb = 0; rb < RRB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[kb][rb][r] = 0.f;
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (kb * 16 + l16) * KS + 32 * ds + 8 * g);
+#pragma unroll
+      for (int rb = 0; rb < RRB; ++rb) sacc[kb][rb] = mfma16(kf, qf[rb][ds], sacc[kb][rb]);
+    }
+}
+
+
+// Dense kernel.  A work-group of 8 waves owns 384 query rows of one (b, h);
+// a tail work-group (with a caller workspace) gets one of the `split` key
+// ranges of its block and stores a partial result instead of O.
+template <int I, int END>
+__device__ __forceinline__ void r_prefetch(bf16x8 (&fr)[kRPre + 1], const __bf16* sK, const __bf16* sV, int l16,
+                                          int g, int s) {
+  if constexpr (I < END) {
+    fr[I % (kRPre + 1)] = r_operand<I>(sK, sV, l16, g, s);
+    r_prefetch<I + 1, END>(fr, sK, sV, l16, g, s);
+  }
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) __bf16 smK[RNB][RBN * KS];
+  __shared__ __attribute__((aligned(16))) __bf16 smV[RNB][RBN * VSR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4, s = lane & 15;
+  int tile, part = -1;
+  if ((int)blockIdx.x < a.nfull) {
+    tile = xcd_remap(blockIdx.x, a.nfull);
+  } else {
+    const int j = blockIdx.x - a.nfull;
+    tile = a.nfull + j / a.split;
+    part = j % a.split;
+  }
+  const int bh = tile / a.nqb, qblk = tile % a.nqb;
+  const int b = bh / a.H, hd = bh % a.H;
+  const int N = a.N;
+  const float c = a.c;
+
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.qs[0] + hd * a.qs[1];
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + b * a.ks[0] + hd * a.ks[1];
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.vs[0] + hd * a.vs[1];
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qp, a.q_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, a.k_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, a.v_bytes);
+  const uint32_t qrow = (uint32_t)(a.qs[2] * 2), krow = (uint32_t)(a.ks[2] * 2),
+                 vrow = (uint32_t)(a.vs[2] * 2);
+
+  // Q as the B operand: lane (g, l16) holds row q0 + 16 rb + l16, d = 32 ds
+  // + 8 g .. +7.  Rows >= N load as zero (row N is past the buffer).
+  const int q0 = qblk * RBM + wave * (16 * RRB);
+  bf16x8 qf[RRB][4];
+#pragma unroll
+  for (int rb = 0; rb < RRB; ++rb)
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      const int row = min(q0 + 16 * rb + l16, N);
+      qf[rb][ds] = __builtin_bit_cast(bf16x8, buf_load_b128(rq, (uint32_t)row * qrow + (32 * ds + 8 * g) * 2));
+    }
+
+  f32x4 oacc[8][RRB];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int rb = 0; rb < RRB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[db][rb][r] = 0.f;
+  RowState st[RRB];
+#pragma unroll
+  for (int rb = 0; rb < RRB; ++rb) st[rb] = {-INFINITY, 0.f, 0.f};
+
+  // Key tiles [t0, t1) of T; part p of `split` takes t = p T / split ..
+  // (p + 1) T / split (never empty: split <= T).
+  const int T = (N + RBN - 1) / RBN;
+  int t0 = 0, t1 = T;
+  if (part >= 0) {
+    t0 = part * T / a.split;
+    t1 = (part + 1) * T / a.split;
+  }
+
+  // ---- prologue: tiles t0 and t0+1 into LDS, t0+2 into registers (loads
+  // past N read as zero; tiles past t1 are never used) ----
+  RLoader ld;
+  ld.load(rk, rv, krow, vrow, t0 * RBN, N, tid);
+  ld.store(smK[0], smV[0], tid);
+  ld.load(rk, rv, krow, vrow, (t0 + 1) * RBN, N, tid);
+  ld.store(smK[1], smV[1], tid);
+  ld.load(rk, rv, krow, vrow, (t0 + 2) * RBN, N, tid);
+  __syncthreads();
+
+  f32x4 sacc[2][RRB];
+  uint32_t pk[RRB][4];
+  r_qk_tile(sacc, smK[0], qf, l16, g);
+  if ((t0 + 1) * RBN > N) r_mask(sacc, t0 * RBN, N, g);
+  r_softmax(sacc, st, oacc, pk, c, true);
+
+  // ---- step t: QK^T of tile t+1 and PV of tile t, barrier, softmax of t+1 ----
+  int bc = 0;
+  for (int t = t0; t + 1 < t1; ++t) {
+    const int bn = (bc + 1 == RNB) ? 0 : bc + 1;
+    const int bn2 = (bn + 1 == RNB) ? 0 : bn + 1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rb = 0; rb < RRB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[kb][rb][r] = 0.f;
+    bf16x8 fr[kRPre + 1];
+    r_prefetch<0, kRPre>(fr, smK[bn], smV[bc], l16, g, s);
+    r_step<0>(sacc, oacc, qf, pk, smK[bn], smV[bc], l16, g, s, fr, ld, smK[bn2], smV[bn2], rk, rv, krow, vrow,
+              (t + 3) * RBN, N, tid);
+    __builtin_amdgcn_sched_group_barrier(0x100, kRPre, 0);
+    r_step_schedule<0>();
+    __syncthreads();
+    const int key1 = (t + 1) * RBN;
+    if (key1 + RBN > N) r_mask(sacc, key1, N, g);
+    r_softmax(sacc, st, oacc, pk, c, false);
+    bc = bn;
+  }
+  // ---- drain: PV of the last tile ----
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const bf16x8 vf = r_v_operand(smV[bc], db, g, s);
+#pragma unroll
+    for (int rb = 0; rb < RRB; ++rb) oacc[db][rb] = mfma16(vf, r_p_operand(pk[rb]), oacc[db][rb]);
+  }
+
+  // ---- epilogue: lane (g, l16) holds d = 16 db + 4 g + r of row q0 + 16 rb + l16 ----
+  const int64_t ob = b * a.os[0] + hd * a.os[1];
+#pragma unroll
+  for (int rb = 0; rb < RRB; ++rb) {
+    const float lt = r_row_sum(st[rb].l);
+    const int row = q0 + 16 * rb + l16;
+    if (row >= N) continue;
+    if (part >= 0) {
+      // Partial result of one key range: unnormalised O, m c and l.
+      float* pr = a.part + ((int64_t)(blockIdx.x - a.nfull) * RBM + wave * (16 * RRB) + 16 * rb + l16) * kPartRow;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(pr + 16 * db + 4 * g) = oacc[db][rb];
+      if (g == 0) {
+        pr[128] = st[rb].mc;
+        pr[129] = lt;
+      }
+      continue;
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int64_t orow = ob + (int64_t)row * a.os[2];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int d0 = 16 * db + 4 * g;
+      const float v0 = oacc[db][rb][0] * inv, v1 = oacc[db][rb][1] * inv;
+      const float v2 = oacc[db][rb][2] * inv, v3 = oacc[db][rb][3] * inv;
+      if constexpr (OUT_F32) {
+        const f32x4 t4 = {v0, v1, v2, v3};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d0) = t4;
+      } else {
+        const u32x2 t2 = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + orow + d0) = t2;
+      }
+    }
+    if (a.lse != nullptr && g == 0)
+      a.lse[(int64_t)bh * N + row] =
+          lt > 0.f ? (st[rb].mc + __builtin_log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+  }
+}
+
 // Combine the partial results of the split tail blocks, one wave per row:
 // M = max_p m_p, w_p = 2^(m_p - M), O = sum_p w_p O_p / sum_p w_p l_p,
 // lse = ln2 (M + log2 l + lse_off), the parts taken in key order (m in log2
@@ -659,14 +900,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnArgs a) {
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int rid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int tail = rid / 256, rr = rid % 256;
+  const int tail = rid / a.bm, rr = rid % a.bm;
   const int tile = a.nfull + tail;
   const int bh = tile / a.nqb, qblk = tile % a.nqb;
   const int b = bh / a.H, hd = bh % a.H;
-  const int row = qblk * 256 + rr;
+  const int row = qblk * a.bm + rr;
   if (row >= a.N) return;
-  const float* base = a.part + ((int64_t)tail * a.split * 256 + rr) * kPartRow;
-  const int64_t pstride = (int64_t)256 * kPartRow;
+  const float* base = a.part + ((int64_t)tail * a.split * a.bm + rr) * kPartRow;
+  const int64_t pstride = (int64_t)a.bm * kPartRow;
   float M = -INFINITY;
   for (int p = 0; p < a.split; ++p) M = fmaxf(M, base[p * pstride + 128]);
   float L = 0.f, o0 = 0.f, o1 = 0.f;
@@ -695,7 +936,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 
 hipError_t launch_attn_merge(const AttnArgs& a, bool out_f32, hipStream_t s) {
   if (a.split <= 1 || a.ntail <= 0) return hipSuccess;
-  const dim3 grid((unsigned)a.ntail * 64);
+  const dim3 grid((unsigned)(a.ntail * a.bm / 4));   // one wave per row, 4 waves per work-group
   if (out_f32) hipLaunchKernelGGL((attn_merge_kernel<true>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((attn_merge_kernel<false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -703,10 +944,19 @@ hipError_t launch_attn_merge(const AttnArgs& a, bool out_f32, hipStream_t s) {
 
 hipError_t launch_attn_bf16(const AttnArgs& args, bool out_f32, bool sparse, hipStream_t s) {
   AttnArgs a = args;
-  a.nqb = sparse ? a.nb : (a.N + 255) / 256;   // work-group rows: 128 (sparse) or 256 (dense)
+  if (sparse) {
+    a.nqb = a.nb;   // one work-group per 128-row mask block
+    const int64_t nwg = (int64_t)a.B * a.H * a.nqb;
+    if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (out_f32) hipLaunchKernelGGL((attn_sparse_kernel<true>), dim3((unsigned)nwg), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_sparse_kernel<false>), dim3((unsigned)nwg), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  a.nqb = (a.N + kDenseRows - 1) / kDenseRows;
+  a.bm = kDenseRows;
   int64_t nwg = (int64_t)a.B * a.H * a.nqb;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (sparse || a.split <= 1 || a.part == nullptr) {
+  if (a.split <= 1 || a.part == nullptr) {
     a.nfull = (int)nwg;
     a.ntail = 0;
     a.split = 1;
@@ -715,17 +965,11 @@ hipError_t launch_attn_bf16(const AttnArgs& args, bool out_f32, bool sparse, hip
     nwg = (int64_t)a.nfull + (int64_t)a.ntail * a.split;
   }
   const dim3 grid((unsigned)nwg);
-  if (sparse) {
-    if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<4, 2, true, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<4, 2, false, true>), grid, dim3(256), 0, s, a);
-  } else {
-    if (out_f32) hipLaunchKernelGGL((attn_bf16_kernel<8, 3, true, false>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<8, 3, false, false>), grid, dim3(512), 0, s, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_attn_merge(a, out_f32, s);
-  }
-  return hipGetLastError();
+  if (out_f32) hipLaunchKernelGGL((attn_dense_kernel<true>), grid, dim3(RNT), 0, s, a);
+  else hipLaunchKernelGGL((attn_dense_kernel<false>), grid, dim3(RNT), 0, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attn_merge(a, out_f32, s);
 }
 
 }  // namespace dit

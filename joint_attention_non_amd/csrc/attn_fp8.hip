@@ -527,6 +527,7 @@ hipError_t launch_attn_fp8(const Fp8Args& args, bool out_f32, hipStream_t s) {
   m.split = a.split;
   m.part = a.part;
   m.lse_off = -8.8073549220576041f;   // -log2(448)
+  m.bm = 256;                          // 8 waves x 32 query rows
   return launch_attn_merge(m, out_f32, s);
 }
 

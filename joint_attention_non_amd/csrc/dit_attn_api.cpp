@@ -119,20 +119,20 @@ int device_cus() {
   return cus;
 }
 
-// Tail split of the dense bf16 grid: one 256-row work-group runs per CU at a
-// time, so B*H*ceil(N/256) work-groups leave a last partial round of r
+// Tail split of a grid of `rows`-row work-groups (one runs per CU at a
+// time): B*H*ceil(N/rows) work-groups leave a last partial round of r
 // blocks.  Each of those is split into `split` key ranges (as many as fill
-// the CUs, at most one per 64-key tile), so the last round costs 1/split of
-// a full one.  No split when there is no partial round or only one block
-// fits per CU.
+// the CUs, at most one per key tile), so the last round costs 1/split of a
+// full one.  No split when there is no partial round or only one block fits
+// per CU.
 struct TailPlan {
   int nfull = 0, ntail = 0, split = 1;
   size_t bytes = 0;
 };
 
-TailPlan tail_plan(const dit_attn_shape* sh, int cus, int tile_keys) {
+TailPlan tail_plan(const dit_attn_shape* sh, int cus, int rows, int tile_keys) {
   TailPlan t;
-  const int64_t units = (int64_t)sh->batch * sh->heads * ((sh->seqlen + 255) / 256);
+  const int64_t units = (int64_t)sh->batch * sh->heads * ((sh->seqlen + rows - 1) / rows);
   t.nfull = (int)units;
   if (cus <= 0 || units > 0x7fffffff) return t;
   const int64_t full_rounds = units / cus, r = units % cus;
@@ -143,7 +143,7 @@ TailPlan tail_plan(const dit_attn_shape* sh, int cus, int tile_keys) {
   t.nfull = (int)(units - r);
   t.ntail = (int)r;
   t.split = (int)split;
-  t.bytes = (size_t)(r * split) * 256 * dit::kPartRow * sizeof(float);
+  t.bytes = (size_t)(r * split) * rows * dit::kPartRow * sizeof(float);
   return t;
 }
 
@@ -159,7 +159,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 Fp8Layout fp8_layout(int64_t BH, int64_t N, const dit_attn_shape* sh) {
   const int64_t nb = (N + 127) / 128, np = nb * 128;
   Fp8Layout L;
-  if (sh != nullptr) L.plan = tail_plan(sh, device_cus(), 128);
+  if (sh != nullptr) L.plan = tail_plan(sh, device_cus(), 256, 128);   // 256-row blocks, 128-key tiles
   const size_t codes = (size_t)(BH * np * 128), scales = (size_t)(BH * nb) * 4;
   L.q8 = 0;
   L.k8 = round256(L.q8 + codes);
@@ -252,7 +252,7 @@ int dit_attn_fwd(const dit_attn_shape* shape, const void* q, const void* k, cons
 
 size_t dit_attn_fwd_workspace_bytes(const dit_attn_shape* shape) {
   if (shape == nullptr || shape->batch < 1 || shape->heads < 1 || shape->seqlen < 1) return 0;
-  return tail_plan(shape, device_cus(), 64).bytes;
+  return tail_plan(shape, device_cus(), dit::kDenseRows, dit::kDenseTileKeys).bytes;
 }
 
 int dit_attn_fwd_ws(const dit_attn_shape* shape, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -260,7 +260,7 @@ int dit_attn_fwd_ws(const dit_attn_shape* shape, const void* q, const void* k, c
   g_err[0] = '\0';
   int rc = check_common(shape, q, k, v, o, lse);
   if (rc) return rc;
-  const TailPlan t = tail_plan(shape, device_cus(), 64);
+  const TailPlan t = tail_plan(shape, device_cus(), dit::kDenseRows, dit::kDenseTileKeys);
   dit::AttnArgs a;
   fill_common(shape, q, k, v, o, lse, a);
   if (t.split > 1) {

@@ -26,9 +26,15 @@ struct AttnArgs {
   // into `split` key ranges whose partial results go to `part` and are
   // combined by the merge kernel.  split == 1: no tail split.
   int nfull, ntail, split;
-  float* part;          // [ntail * split][256 rows][kPartRow] fp32
+  float* part;          // [ntail * split][bm rows][kPartRow] fp32
   float lse_off;        // added to log2 of the merged weight sum (0; fp8: -log2 448)
+  int bm;               // query rows per block of the split grid (merge)
 };
+
+// Dense bf16 kernel: query rows per work-group and keys per LDS tile (the
+// host's tail-split plan works in these units).
+constexpr int kDenseRows = 384;
+constexpr int kDenseTileKeys = 32;
 
 // fp32 words per row of a partial result: 128 unnormalised O, the row's
 // reference m c (log2 units), its weight sum l, and two words of padding.
@@ -54,7 +60,7 @@ struct Fp8Args {
   float p_off;          // just below log2(448): w * 448 = exp2(x + p_off) <= 448
   // Tail split of the attention grid, as for AttnArgs (split == 1: none).
   int nfull, ntail, split;
-  float* part;          // [ntail * split][256 rows][kPartRow] fp32
+  float* part;          // [ntail * split][bm rows][kPartRow] fp32
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool out_f32, bool sparse, hipStream_t s);

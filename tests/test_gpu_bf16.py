@@ -89,10 +89,11 @@ def test_bitwise_determinism():
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
 
-# (query row, dominant key) pairs for N = 300 (tiles of 64 keys, the last one
-# ragged): the key sits in either half of the 32-key accumulator blocks
-# (key % 8 < 4 or >= 4), in either block of its tile, in the first, a middle
-# and the ragged last tile, and the rows cover several waves.
+# (query row, dominant key) pairs for N = 300 (the dense kernel's 32-key
+# tiles, the last one ragged): the key sits in each of the four 4-key lane
+# groups (key % 16 // 4) and in both 16-key halves of its tile, in the
+# first, a middle and the ragged last tile, and the rows cover several
+# waves and 16-row blocks.
 ONE_HOT_CASES = [(17, 250), (3, 68), (40, 36), (63, 299), (100, 270), (299, 7), (150, 131), (255, 190)]
 
 

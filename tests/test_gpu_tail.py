@@ -1,5 +1,5 @@
 """GPU parity of dit_attn_fwd_ws: the dense bf16 attention with the last,
-partial round of 256-row query blocks split over key ranges and merged.
+partial round of 384-row query blocks split over key ranges and merged.
 
 Every expected value comes from ``oracle/`` on the same seeded inputs; the
 rows outside the split blocks must equal dit_attn_fwd's output bit for bit.
@@ -24,13 +24,16 @@ def _say(msg):
     print(msg, flush=True)
 
 
+ROWS, TILE = 384, 32   # dense work-group rows and keys per tile
+
+
 def _plan(B, H, N):
     """(first split block, blocks split, parts per block) as the library
-    plans it: one 256-row block per compute unit at a time."""
+    plans it: one 384-row block per compute unit at a time."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    units = B * H * ((N + 255) // 256)
+    units = B * H * ((N + ROWS - 1) // ROWS)
     full, r = divmod(units, cus)
-    split = min(cus // r, (N + 63) // 64) if (full >= 1 and r > 0) else 1
+    split = min(cus // r, (N + TILE - 1) // TILE) if (full >= 1 and r > 0) else 1
     if split < 2:
         return units, 0, 1
     return units - r, r, split
@@ -38,11 +41,11 @@ def _plan(B, H, N):
 
 def _tail_rows(B, H, N, first):
     """Flat row ids (bh * N + i) of the query blocks from `first` on."""
-    nqb = (N + 255) // 256
+    nqb = (N + ROWS - 1) // ROWS
     rows = []
     for u in range(first, B * H * nqb):
         bh, qb = divmod(u, nqb)
-        lo, hi = qb * 256, min(qb * 256 + 256, N)
+        lo, hi = qb * ROWS, min(qb * ROWS + ROWS, N)
         rows.append(torch.arange(bh * N + lo, bh * N + hi))
     return torch.cat(rows) if rows else torch.zeros(0, dtype=torch.int64)
 
@@ -75,7 +78,7 @@ def test_img2048_split_tail_parity_and_untouched_rows():
     q, k, v, _ = make_workload_inputs(w, seed=0)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     need = dit.fwd_workspace_bytes(qd)
-    assert need == ntail * split * 256 * 132 * 4
+    assert need == ntail * split * ROWS * 132 * 4
     ws = dit.fwd_workspace(qd)
     o16, o32, lse = _run_ws(qd, kd, vd, ws)
     assert torch.equal(rne_bf16(o32).view(torch.int16), o16.view(torch.int16))
@@ -96,14 +99,14 @@ def test_img2048_split_tail_parity_and_untouched_rows():
 
 def test_ragged_split_tail_parity_one_hot_and_determinism():
     B, H = 1, 1
-    N = 256 * 300 - 77
+    N = ROWS * 300 - 77
     first, ntail, split = _plan(B, H, N)
     _say(f"case: ragged N={N} split plan first={first} tail={ntail} split={split}")
     assert ntail > 0 and split >= 2
     q, k, v = make_qkv(B, H, N, 128, seed=51)
     # A dominant key for one query row inside a split block: P = 1 for it,
     # every other weight of the row underflows, so O is that V row exactly.
-    i, j = first * 256 + 100, 3000
+    i, j = first * ROWS + 100, 3000
     k[0, 0, j] = (40.0 * q[0, 0, i].float()).to(torch.bfloat16)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     ws = dit.fwd_workspace(qd)
@@ -116,7 +119,7 @@ def test_ragged_split_tail_parity_one_hot_and_determinism():
     tail = _tail_rows(B, H, N, first)
     g = torch.Generator().manual_seed(52)
     pick = tail[torch.randperm(tail.numel(), generator=g)[:48]]
-    rows = torch.unique(torch.cat([pick, torch.tensor([i, N - 1, N - 2, first * 256 - 1, 0])]))
+    rows = torch.unique(torch.cat([pick, torch.tensor([i, N - 1, N - 2, first * ROWS - 1, 0])]))
     rows = rows[rows != i]
     _check_rows(o16, o32, lse, q, k, v, rows, 1.0 / math.sqrt(128))
 
