@@ -1,15 +1,8 @@
 // attn_bf16.hip -- bf16 flash-style joint attention forward for gfx950.
 //
-// A work-group of NW waves owns 32 * NW query rows of one (batch, head); each
-// wave owns 32 rows.  K and V stream through LDS in tiles of 64 keys, in
-// three rotating buffers: while tile t is finished, tile t+1 is already in
-// LDS and tile t+2 is being stored from registers loaded one step earlier.
-//
-// Per tile and wave, with the 32x32x16 bf16 MFMA (fp32 accumulate):
-//   S^T = K Q^T      A = K rows from LDS, B = Q held in registers.  In the
-//                    transposed product each lane holds 16 keys of one query
-//                    row, so the row max and row sum are in-register
-//                    reductions plus one exchange with lane l^32.
+// Both kernels follow one recipe per key tile (fp32 accumulate):
+//   S^T = K Q^T      A = K rows from LDS, B = Q held in registers for the
+//                    whole kernel.
 //   online softmax   P = 2^(S c - m c) with c = scale * log2(e) and m a
 //                    running reference: the row max of the first tile.  Later
 //                    tiles take their exponentials against it directly; only
@@ -26,26 +19,32 @@
 //                    transposing read fetches to match the order in which
 //                    the accumulator hands P out.  l accumulates the same
 //                    rounded P (v_dot2 with (1, 1)).
-// Software pipeline: step t issues the QK^T MFMAs of tile t+1 and the PV
-// MFMAs of tile t as one stream with their LDS operands read six MFMAs
-// ahead; the LDS stores of tile t+2 and the global loads of tile t+3 ride
-// on the PV MFMAs; then one barrier, then the softmax of tile t+1.
 // Epilogue: O = O^T / l, stored bf16 (round to nearest even) or fp32, and
 // optionally lse = ln2 * (m c + log2 l).
 //
-// The block-sparse variant runs the same per-tile arithmetic over the active
-// 128-key blocks of its query block only (masked blocks are never loaded),
-// with two LDS buffers and its global loads issued two steps ahead in two
-// alternating register sets.
+// Dense kernel (attn_dense_kernel): 8 waves x 48 query rows = 384 rows of
+// one (batch, head) per work-group, two waves per SIMD.  Each wave's rows are
+// three 16-row blocks on the 16x16x32 bf16 MFMA, so every K fragment and V
+// operand read from LDS feeds three MFMAs (a third less LDS traffic per flop
+// than 32-row waves).  K and V stream through LDS in 32-key tiles in three
+// rotating buffers.  Step t issues the QK^T MFMAs of tile t+1 and the PV
+// MFMAs of tile t as one stream with their LDS operands read ahead; the LDS
+// stores of tile t+2 and the global loads of tile t+3 ride on the PV MFMAs;
+// then one barrier, then the softmax of tile t+1.
 //
-// Tail split (dense, with a caller workspace): one 256-row work-group runs
+// Tail split (dense, with a caller workspace): one 384-row work-group runs
 // per compute unit at a time, so the query blocks of a last, partial round
 // would leave most units idle.  Each of those blocks is instead split into
 // `split` consecutive key ranges run by separate work-groups (launched after
 // the full blocks); each range stores its unnormalised O, reference m c and
 // weight sum l, and attn_merge_kernel combines them in key order with the
 // exact rescaling 2^(m_p c - max m c).
-#include <type_traits>
+//
+// Block-sparse kernel (attn_sparse_kernel): 4 waves x 32 rows = one 128-row
+// mask block per work-group (two per CU), 32x32x16 MFMAs, 64-key tiles over
+// the kept 128-key blocks of its mask row only (masked blocks are never
+// loaded), two LDS buffers, and its global loads issued two steps ahead in
+// two alternating register sets.
 
 #include "device_common.h"
 #include "launch.h"
@@ -54,7 +53,7 @@ namespace dit {
 namespace {
 
 constexpr int D = kHeadDim;
-constexpr int BN = 64;        // keys per LDS tile
+constexpr int BN = 64;        // keys per LDS tile (block-sparse kernel)
 constexpr int KS = D + 8;     // K tile row stride in bf16 (272 B: conflict-free b128 reads)
 constexpr int VSR = D + 32;   // V tile row stride in bf16 (320 B: 4 consecutive rows of a
                               // transposing read land in disjoint bank quarters)
@@ -524,6 +523,18 @@ __global__ __launch_bounds__(256, 2) void attn_sparse_kernel(AttnArgs a) {
 }
 
 // ---- dense kernel: 48 query rows per wave on the 16x16x32 MFMA ----
+//
+// Per 32-key tile and wave (lane = 16 g + l16):
+//   S^T = K Q^T      A = K (16 keys x 32 d) from LDS, B = Q^T (32 d x 16 rows)
+//                    in registers; the accumulator gives lane (g, l16) keys
+//                    4 g + r of query row l16 of each 16-row block, and each
+//                    K fragment feeds the three row blocks.
+//   O^T += V^T P^T   A = V^T (16 d x 32 keys) by two transposing LDS reads
+//                    (keys 4g..4g+3 and 16+4g..16+4g+3 for lane group g), B =
+//                    P packed from the S registers in the same key order;
+//                    each V operand feeds the three row blocks.
+// A query row's keys are spread over the four lane groups, so its row max
+// and sum take two exchanges (lanes l^16, then l^32).
 
 constexpr int RBN = 32;                 // keys per tile
 constexpr int RNB = 3;                  // LDS tile buffers
