@@ -543,6 +543,11 @@ constexpr int RNW = 8;                  // waves per work-group
 constexpr int RBM = RNW * 16 * RRB;     // 384 query rows per work-group
 static_assert(RBM == kDenseRows && RBN == kDenseTileKeys, "the host plans with these sizes");
 constexpr int RNT = RNW * 64;
+// V tile row stride in bf16: 288 B (72 banks).  A transposing read covers
+// rows 4g .. 4g+3 for each lane group g; with 72 r mod 64 = 8 r the rows of
+// groups 0 and 1 (and of 2 and 3) use disjoint banks.  Measured: half the
+// bank-conflict cycles of 64-bank strides of 68, 76, 80, 84 or 92 (88 ties).
+constexpr int RVS = D + 16;
 
 struct RLoader {
   // 32 keys x 16 chunks of 16 bytes, for K (I = 0) and V (I = 1).
@@ -557,7 +562,7 @@ struct RLoader {
   template <int I>
   __device__ __forceinline__ void store_one(__bf16* sk, __bf16* sv, int tid) const {
     const int key = tid >> 4, c = tid & 15;
-    *reinterpret_cast<u32x4*>((I == 0 ? sk + key * KS : sv + key * VSR) + c * 8) = r[I];
+    *reinterpret_cast<u32x4*>((I == 0 ? sk + key * KS : sv + key * RVS) + c * 8) = r[I];
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t krow,
                                        uint32_t vrow, int key0, int N, int tid) {
@@ -578,11 +583,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // rows 16 kb + l % 16, d 32 ds + 8 g .. +7.  J >= 8 -> V^T operand, d block
 // db = J - 8: lane (g, s) reads rows 4g + s/4 (+16), columns 16 db + 4 (s%4).
 __device__ __forceinline__ bf16x8 r_v_operand(const __bf16* sV, int db, int g, int s) {
-  const __bf16* base = sV + (4 * g + (s >> 2)) * VSR + 16 * db + 4 * (s & 3);
+  const __bf16* base = sV + (4 * g + (s >> 2)) * RVS + 16 * db + 4 * (s & 3);
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base));
   const s16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + 16 * VSR));
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + 16 * RVS));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
@@ -760,7 +765,7 @@ __device__ __forceinline__ void r_prefetch(bf16x8 (&fr)[kRPre + 1], const __bf16
 template <bool OUT_F32>
 __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 smK[RNB][RBN * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 smV[RNB][RBN * VSR];
+  __shared__ __attribute__((aligned(16))) __bf16 smV[RNB][RBN * RVS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4, s = lane & 15;
