@@ -92,7 +92,8 @@ size_t dit_attn_fwd_workspace_bytes(const dit_attn_shape* shape);
 /* The same attention as dit_attn_fwd (same operation, same arguments and
  * errors), with a caller workspace for load balancing: the query blocks of
  * 384 rows run one per compute unit, and those of the last, partial round
- * are each split into key ranges whose partial results (own running max,
+ * (the whole grid, if it is smaller than one round) are each split into key
+ * ranges whose partial results (own running max,
  * unnormalised O and weight sum) are combined by a second kernel in key
  * order: O = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p with M = max m_p.
  * The workspace (device memory, 256-byte aligned, caller-owned, at least

@@ -123,21 +123,24 @@ int device_cus() {
 // time): B*H*ceil(N/rows) work-groups leave a last partial round of r
 // blocks.  Each of those is split into `split` key ranges (as many as fill
 // the CUs, at most one per key tile), so the last round costs 1/split of a
-// full one.  No split when there is no partial round or only one block fits
-// per CU.
+// full one.  With `small`, a grid smaller than one round is all partial
+// round and is split the same way (the bf16 path; the fp8 path keeps such
+// grids whole, so their rows follow the one-pass recipe).  No split when the
+// grid is whole rounds, or when more than half the CUs are busy in the last
+// round (split < 2).
 struct TailPlan {
   int nfull = 0, ntail = 0, split = 1;
   size_t bytes = 0;
 };
 
-TailPlan tail_plan(const dit_attn_shape* sh, int cus, int rows, int tile_keys) {
+TailPlan tail_plan(const dit_attn_shape* sh, int cus, int rows, int tile_keys, bool small) {
   TailPlan t;
   const int64_t units = (int64_t)sh->batch * sh->heads * ((sh->seqlen + rows - 1) / rows);
   t.nfull = (int)units;
   if (cus <= 0 || units > 0x7fffffff) return t;
-  const int64_t full_rounds = units / cus, r = units % cus;
+  const int64_t r = units % cus;
   const int64_t tiles = (sh->seqlen + tile_keys - 1) / tile_keys;
-  if (full_rounds < 1 || r == 0) return t;
+  if (r == 0 || (!small && units < cus)) return t;
   const int64_t split = std::min<int64_t>(cus / r, tiles);
   if (split < 2) return t;
   t.nfull = (int)(units - r);
@@ -159,7 +162,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 Fp8Layout fp8_layout(int64_t BH, int64_t N, const dit_attn_shape* sh) {
   const int64_t nb = (N + 127) / 128, np = nb * 128;
   Fp8Layout L;
-  if (sh != nullptr) L.plan = tail_plan(sh, device_cus(), 256, 128);   // 256-row blocks, 128-key tiles
+  if (sh != nullptr) L.plan = tail_plan(sh, device_cus(), 256, 128, false);   // 256-row blocks, 128-key tiles
   const size_t codes = (size_t)(BH * np * 128), scales = (size_t)(BH * nb) * 4;
   L.q8 = 0;
   L.k8 = round256(L.q8 + codes);
@@ -252,7 +255,7 @@ int dit_attn_fwd(const dit_attn_shape* shape, const void* q, const void* k, cons
 
 size_t dit_attn_fwd_workspace_bytes(const dit_attn_shape* shape) {
   if (shape == nullptr || shape->batch < 1 || shape->heads < 1 || shape->seqlen < 1) return 0;
-  return tail_plan(shape, device_cus(), dit::kDenseRows, dit::kDenseTileKeys).bytes;
+  return tail_plan(shape, device_cus(), dit::kDenseRows, dit::kDenseTileKeys, true).bytes;
 }
 
 int dit_attn_fwd_ws(const dit_attn_shape* shape, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -260,7 +263,7 @@ int dit_attn_fwd_ws(const dit_attn_shape* shape, const void* q, const void* k, c
   g_err[0] = '\0';
   int rc = check_common(shape, q, k, v, o, lse);
   if (rc) return rc;
-  const TailPlan t = tail_plan(shape, device_cus(), dit::kDenseRows, dit::kDenseTileKeys);
+  const TailPlan t = tail_plan(shape, device_cus(), dit::kDenseRows, dit::kDenseTileKeys, true);
   dit::AttnArgs a;
   fill_common(shape, q, k, v, o, lse, a);
   if (t.split > 1) {

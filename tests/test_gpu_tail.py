@@ -32,8 +32,8 @@ def _plan(B, H, N):
     plans it: one 384-row block per compute unit at a time."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     units = B * H * ((N + ROWS - 1) // ROWS)
-    full, r = divmod(units, cus)
-    split = min(cus // r, (N + TILE - 1) // TILE) if (full >= 1 and r > 0) else 1
+    r = units % cus
+    split = min(cus // r, (N + TILE - 1) // TILE) if r > 0 else 1
     if split < 2:
         return units, 0, 1
     return units - r, r, split
@@ -124,8 +124,25 @@ def test_ragged_split_tail_parity_one_hot_and_determinism():
     _check_rows(o16, o32, lse, q, k, v, rows, 1.0 / math.sqrt(128))
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 2, 4000), (1, 2, 320)])
+def test_small_grid_split_full_parity(B, H, N):
+    """A grid smaller than one round is split as a whole (every block over
+    several key ranges); full parity against the oracle."""
+    first, ntail, split = _plan(B, H, N)
+    _say(f"case: small grid B{B} H{H} N{N} plan first={first} tail={ntail} split={split}")
+    assert first == 0 and ntail > 0 and split >= 2
+    q, k, v = make_qkv(B, H, N, 128, seed=55)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    ws = dit.fwd_workspace(qd)
+    o16, o32, lse = _run_ws(qd, kd, vd, ws)
+    assert torch.equal(rne_bf16(o32).view(torch.int16), o16.view(torch.int16))
+    _check_rows(o16, o32, lse, q, k, v, torch.arange(B * H * N), 1.0 / math.sqrt(128))
+
+
 def test_no_split_shapes_match_dit_attn_fwd_bitwise():
-    for (B, H, N) in ((1, 2, 320), (1, 24, 4608)):
+    # whole rounds on 256 CUs (16 x 16 blocks of 384 rows), and a grid that
+    # keeps more than half the CUs busy (1 x 160 blocks)
+    for (B, H, N) in ((1, 16, 6144), (1, 1, 384 * 160)):
         first, ntail, split = _plan(B, H, N)
         _say(f"case: B{B} H{H} N{N} plan tail={ntail} split={split}")
         q, k, v = (t.to(DEV) for t in make_qkv(B, H, N, 128, seed=53))
