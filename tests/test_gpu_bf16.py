@@ -76,8 +76,13 @@ def test_strided_bnhd_layout_matches_contiguous_bitwise():
     assert qs.stride(2) == 4 * 128
     o_strided = dit.attn_fwd(qs, ks, vs)
     o_contig = dit.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV))
+    # the workspace entry point splits this small grid over key ranges; the
+    # strides must not matter there either
+    o_ws_strided = dit.attn_fwd(qs, ks, vs, workspace=dit.fwd_workspace(qs))
+    o_ws_contig = dit.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), workspace=dit.fwd_workspace(qs))
     torch.cuda.synchronize()
     assert torch.equal(o_strided.view(torch.int16), o_contig.view(torch.int16))
+    assert torch.equal(o_ws_strided.view(torch.int16), o_ws_contig.view(torch.int16))
 
 
 def test_bitwise_determinism():
