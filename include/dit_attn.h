@@ -153,22 +153,35 @@ int dit_attn_fp8_quantize(const dit_attn_shape* shape,
                           const void* q, const void* k, const void* v,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes dit_attn_fwd_blocksparse needs for `shape` on the current
+ * device.  This build's block-sparse kernel keeps no state between its
+ * work-groups, so the answer is 0 for every shape (the workspace may then be
+ * NULL); callers should still ask, so that a later build can use the
+ * workspace (for an active-block list, for instance) without an ABI change. */
+size_t dit_attn_fwd_blocksparse_workspace_bytes(const dit_attn_shape* shape);
+
 /* Block-sparse bf16 attention over 128x128 (query block, key block) tiles
  * (the "blokksparse" attention backend, bpdata.com page, section "Mi
  * szerepel az optimalizálásban").  block_mask is a device uint8 array
  * [ceil(N/128)][ceil(N/128)], row = query block, column = key block, nonzero
  * = attend.  Masked blocks act as -inf logits: they are skipped and their K
  * and V are never read.  mask_stride_bh is the element offset between the
- * masks of consecutive (b, h) slices (b-major); 0 shares one mask.
- * block_size must be 128.  The per-tile arithmetic is that of dit_attn_fwd
- * (fp32 scores, P rounded to bf16, row sums over the rounded P) in 64-key
- * tiles on 128-row blocks, so an all-ones mask reproduces dit_attn_fwd
- * within the same tolerance, not bit for bit. */
+ * masks of consecutive (b, h) slices (b-major); 0 shares one mask.  The
+ * mask's size cannot be checked here: the caller guarantees that
+ * (B*H - 1) * mask_stride_bh + nb * nb bytes are readable.
+ * block_size must be 128.  workspace / workspace_bytes: device memory of at
+ * least dit_attn_fwd_blocksparse_workspace_bytes(shape) bytes, 256-byte
+ * aligned (NULL when that is 0); ERR_WORKSPACE otherwise.
+ * The per-tile arithmetic is that of dit_attn_fwd (fp32 scores, P rounded
+ * to bf16, row sums over the rounded P) in 64-key tiles on 128-row blocks,
+ * so an all-ones mask reproduces dit_attn_fwd within the same tolerance, not
+ * bit for bit. */
 int dit_attn_fwd_blocksparse(const dit_attn_shape* shape,
                              const void* q, const void* k, const void* v,
                              void* o, float* lse,
                              const uint8_t* block_mask, int64_t mask_stride_bh,
-                             int32_t block_size, void* stream);
+                             int32_t block_size,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* dit_attn_status_string(int status);

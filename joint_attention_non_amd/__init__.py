@@ -5,9 +5,10 @@ kernels of ``libdit_attn.so``.  PyTorch supplies device memory and the
 current stream.  There is no fallback: if the library is not built, or a
 call fails, an exception is raised.
 
-    attn_fwd(q, k, v, scale=None, return_lse=False, out_fp32=False, workspace=None)
-    attn_fwd_fp8(q, k, v, scale=None, return_lse=False, workspace=None, out_fp32=False)
-    attn_fwd_blocksparse(q, k, v, block_mask, scale=None, return_lse=False, out_fp32=False)
+    attn_fwd(q, k, v, scale=None, return_lse=False, out_fp32=False, out=None, workspace=None, lse_out=None)
+    attn_fwd_fp8(q, k, v, scale=None, return_lse=False, workspace=None, out_fp32=False, out=None, lse_out=None)
+    attn_fwd_blocksparse(q, k, v, block_mask, scale=None, return_lse=False, out_fp32=False, out=None,
+                         workspace=None, lse_out=None)
     fp8_quantize(q, k, v, workspace=None) -> Fp8Workspace views
 
 q, k, v: CUDA (HIP) bfloat16 tensors [B, H, N, 128] whose last dimension is
@@ -23,7 +24,8 @@ import os
 import torch
 
 __all__ = ["attn_fwd", "attn_fwd_fp8", "attn_fwd_blocksparse", "fp8_quantize",
-           "fp8_workspace_bytes", "fwd_workspace_bytes", "fwd_workspace", "DitAttnError",
+           "fp8_workspace_bytes", "fwd_workspace_bytes", "fwd_workspace",
+           "blocksparse_workspace_bytes", "DitAttnError",
            "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,8 +74,10 @@ def load():
         lib.dit_attn_fwd_fp8.restype = ctypes.c_int
         lib.dit_attn_fp8_quantize.argtypes = [sp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.dit_attn_fp8_quantize.restype = ctypes.c_int
+        lib.dit_attn_fwd_blocksparse_workspace_bytes.argtypes = [sp]
+        lib.dit_attn_fwd_blocksparse_workspace_bytes.restype = ctypes.c_size_t
         lib.dit_attn_fwd_blocksparse.argtypes = [sp, vp, vp, vp, vp, vp, vp, ctypes.c_int64,
-                                                 ctypes.c_int32, vp]
+                                                 ctypes.c_int32, vp, ctypes.c_size_t, vp]
         lib.dit_attn_fwd_blocksparse.restype = ctypes.c_int
         lib.dit_attn_status_string.argtypes = [ctypes.c_int]
         lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -100,7 +104,7 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _shape(q, k, v, o, scale, flags) -> _Shape:
+def _check_inputs(q, k, v):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, N, D], got {tuple(t.shape)}")
@@ -112,6 +116,12 @@ def _shape(q, k, v, o, scale, flags) -> _Shape:
             raise ValueError(f"{name} must have a contiguous last dimension")
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+
+
+def _shape(q, k, v, o, scale, flags) -> _Shape:
+    _check_inputs(q, k, v)
     B, H, N, D = q.shape
     s = _Shape()
     s.batch, s.heads, s.seqlen, s.head_dim = B, H, N, D
@@ -122,13 +132,43 @@ def _shape(q, k, v, o, scale, flags) -> _Shape:
     return s
 
 
-def _outputs(q, return_lse, out_fp32, out=None):
+def _outputs(q, return_lse, out_fp32, out=None, lse_out=None):
+    """Output tensors: caller-supplied ones are checked against what the
+    kernels will write (the C ABI cannot see an allocation's size), missing
+    ones are allocated."""
+    _check_inputs(q, q, q)
     B, H, N, D = q.shape
+    dtype = torch.float32 if out_fp32 else torch.bfloat16
     if out is None:
-        out = torch.empty((B, H, N, D), device=q.device,
-                          dtype=torch.float32 if out_fp32 else torch.bfloat16)
-    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if return_lse else None
+        out = torch.empty((B, H, N, D), device=q.device, dtype=dtype)
+    else:
+        if not isinstance(out, torch.Tensor) or not out.is_cuda or out.device != q.device:
+            raise ValueError("out must be a device tensor on q's device")
+        if tuple(out.shape) != (B, H, N, D):
+            raise ValueError(f"out must have shape {(B, H, N, D)}, got {tuple(out.shape)}")
+        if out.dtype != dtype:
+            raise ValueError(f"out must be {dtype} (out_fp32={out_fp32}), got {out.dtype}")
+        if out.stride(3) != 1:
+            raise ValueError("out must have a contiguous last dimension")
+    lse = None
+    if return_lse or lse_out is not None:
+        if lse_out is None:
+            lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+        else:
+            if (not isinstance(lse_out, torch.Tensor) or not lse_out.is_cuda or lse_out.device != q.device
+                    or lse_out.dtype != torch.float32 or tuple(lse_out.shape) != (B, H, N)
+                    or not lse_out.is_contiguous()):
+                raise ValueError(f"lse_out must be a contiguous float32 device tensor of shape {(B, H, N)}")
+            lse = lse_out
     return out, lse
+
+
+def _check_workspace(ws, q, name="workspace"):
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != q.device:
+        raise ValueError(f"{name} must be a device tensor on q's device")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous uint8 tensor")
+    return ws
 
 
 def fwd_workspace_bytes(q) -> int:
@@ -140,21 +180,26 @@ def fwd_workspace_bytes(q) -> int:
     return int(load().dit_attn_fwd_workspace_bytes(ctypes.byref(s)))
 
 
-def attn_fwd(q, k, v, scale=None, return_lse=False, out_fp32=False, out=None, workspace=None):
+def _ret(o, lse, return_lse):
+    return (o, lse) if return_lse else o
+
+
+def attn_fwd(q, k, v, scale=None, return_lse=False, out_fp32=False, out=None, workspace=None,
+             lse_out=None):
     """Dense bf16 joint attention; returns O (and lse if asked).  With a
     workspace (uint8 device tensor of at least fwd_workspace_bytes(q) bytes)
     the last partial round of query blocks is split over key ranges
-    (dit_attn_fwd_ws)."""
-    o, lse = _outputs(q, return_lse, out_fp32, out)
+    (dit_attn_fwd_ws).  `out` / `lse_out` receive the results when given."""
+    o, lse = _outputs(q, return_lse, out_fp32, out, lse_out)
     s = _shape(q, k, v, o, scale, FLAG_OUT_F32 if out_fp32 else 0)
     if workspace is None:
         _check(load().dit_attn_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                    _stream()), "dit_attn_fwd")
     else:
+        _check_workspace(workspace, q)
         _check(load().dit_attn_fwd_ws(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                      _stream()), "dit_attn_fwd_ws")
-    return (o, lse) if return_lse else o
+                                      _ptr(workspace), workspace.numel(), _stream()), "dit_attn_fwd_ws")
+    return _ret(o, lse, return_lse)
 
 
 def fwd_workspace(q):
@@ -162,20 +207,51 @@ def fwd_workspace(q):
     return torch.empty(max(fwd_workspace_bytes(q), 256), dtype=torch.uint8, device=q.device)
 
 
+def blocksparse_workspace_bytes(q) -> int:
+    """Bytes of workspace dit_attn_fwd_blocksparse needs for q's shape."""
+    B, H, N, D = q.shape
+    s = _Shape()
+    s.batch, s.heads, s.seqlen, s.head_dim = B, H, N, D
+    return int(load().dit_attn_fwd_blocksparse_workspace_bytes(ctypes.byref(s)))
+
+
+def _mask_stride(block_mask, q, block_size):
+    """Element offset between consecutive (b, h) masks; refuses a mask that
+    does not cover every (b, h) slice with [nb, nb] entries."""
+    if (not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8
+            or not block_mask.is_cuda or block_mask.device != q.device or not block_mask.is_contiguous()):
+        raise ValueError("block_mask must be a contiguous uint8 tensor on q's device")
+    B, H, N, _ = q.shape
+    nb = (N + block_size - 1) // block_size if block_size > 0 else 0
+    if block_mask.dim() < 2 or tuple(block_mask.shape[-2:]) != (nb, nb):
+        raise ValueError(f"block_mask must end in [{nb}, {nb}] (ceil(N / {block_size})), "
+                         f"got {tuple(block_mask.shape)}")
+    lead = tuple(block_mask.shape[:-2])
+    if lead == ():
+        return 0
+    if lead in ((B * H,), (B, H)):
+        return nb * nb
+    raise ValueError(f"block_mask must be [nb, nb], [B*H, nb, nb] or [B, H, nb, nb] with B*H = {B * H}, "
+                     f"got {tuple(block_mask.shape)}")
+
+
 def attn_fwd_blocksparse(q, k, v, block_mask, scale=None, return_lse=False, out_fp32=False,
-                         block_size=128, out=None):
+                         block_size=128, out=None, workspace=None, lse_out=None):
     """Block-sparse attention.  block_mask: uint8 device tensor [nb, nb]
     (shared by all heads) or [B, H, nb, nb] / [B*H, nb, nb]."""
-    o, lse = _outputs(q, return_lse, out_fp32, out)
+    o, lse = _outputs(q, return_lse, out_fp32, out, lse_out)
     s = _shape(q, k, v, o, scale, FLAG_OUT_F32 if out_fp32 else 0)
-    if block_mask.dtype != torch.uint8 or not block_mask.is_cuda or not block_mask.is_contiguous():
-        raise ValueError("block_mask must be a contiguous uint8 device tensor")
-    nb2 = block_mask.shape[-1] * block_mask.shape[-2]
-    stride_bh = 0 if block_mask.dim() == 2 else nb2
+    stride_bh = _mask_stride(block_mask, q, block_size)
+    need = blocksparse_workspace_bytes(q)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check_workspace(workspace, q)
     _check(load().dit_attn_fwd_blocksparse(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                            _ptr(lse), _ptr(block_mask), stride_bh, block_size,
+                                           _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                            _stream()), "dit_attn_fwd_blocksparse")
-    return (o, lse) if return_lse else o
+    return _ret(o, lse, return_lse)
 
 
 def fp8_workspace_bytes(q) -> int:
@@ -189,18 +265,18 @@ def _workspace(q, workspace):
     need = fp8_workspace_bytes(q)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    return workspace
+    return _check_workspace(workspace, q)
 
 
-def attn_fwd_fp8(q, k, v, scale=None, return_lse=False, workspace=None, out_fp32=False, out=None):
+def attn_fwd_fp8(q, k, v, scale=None, return_lse=False, workspace=None, out_fp32=False, out=None,
+                 lse_out=None):
     """fp8 (e4m3) joint attention with on-device dynamic per-block scaling."""
-    o, lse = _outputs(q, return_lse, out_fp32, out)
+    o, lse = _outputs(q, return_lse, out_fp32, out, lse_out)
     s = _shape(q, k, v, o, scale, FLAG_OUT_F32 if out_fp32 else 0)
     ws = _workspace(q, workspace)
     _check(load().dit_attn_fwd_fp8(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                   _ptr(ws), ws.numel() * ws.element_size(), _stream()),
-           "dit_attn_fwd_fp8")
-    return (o, lse) if return_lse else o
+                                   _ptr(ws), ws.numel(), _stream()), "dit_attn_fwd_fp8")
+    return _ret(o, lse, return_lse)
 
 
 @dataclasses.dataclass
@@ -244,7 +320,7 @@ def fp8_quantize(q, k, v, workspace=None) -> Fp8Workspace:
     s = _shape(q, k, v, q, None, 0)
     ws = _workspace(q, workspace)
     _check(load().dit_attn_fp8_quantize(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(ws),
-                                        ws.numel() * ws.element_size(), _stream()),
+                                        ws.numel(), _stream()),
            "dit_attn_fp8_quantize")
     return fp8_workspace_views(q, ws)
 

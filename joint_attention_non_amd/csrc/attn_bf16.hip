@@ -953,9 +953,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 hipError_t launch_attn_merge(const AttnArgs& a, bool out_f32, hipStream_t s) {
   if (a.split <= 1 || a.ntail <= 0) return hipSuccess;
   const dim3 grid((unsigned)(a.ntail * a.bm / 4));   // one wave per row, 4 waves per work-group
-  if (out_f32) hipLaunchKernelGGL((attn_merge_kernel<true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((attn_merge_kernel<false>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(out_f32 ? attn_merge_kernel<true> : attn_merge_kernel<false>, grid, dim3(256), s, a);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& args, bool out_f32, bool sparse, hipStream_t s) {
@@ -964,9 +962,8 @@ hipError_t launch_attn_bf16(const AttnArgs& args, bool out_f32, bool sparse, hip
     a.nqb = a.nb;   // one work-group per 128-row mask block
     const int64_t nwg = (int64_t)a.B * a.H * a.nqb;
     if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (out_f32) hipLaunchKernelGGL((attn_sparse_kernel<true>), dim3((unsigned)nwg), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_sparse_kernel<false>), dim3((unsigned)nwg), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_kernel(out_f32 ? attn_sparse_kernel<true> : attn_sparse_kernel<false>, dim3((unsigned)nwg),
+                         dim3(256), s, a);
   }
   a.nqb = (a.N + kDenseRows - 1) / kDenseRows;
   a.bm = kDenseRows;
@@ -981,9 +978,8 @@ hipError_t launch_attn_bf16(const AttnArgs& args, bool out_f32, bool sparse, hip
     nwg = (int64_t)a.nfull + (int64_t)a.ntail * a.split;
   }
   const dim3 grid((unsigned)nwg);
-  if (out_f32) hipLaunchKernelGGL((attn_dense_kernel<true>), grid, dim3(RNT), 0, s, a);
-  else hipLaunchKernelGGL((attn_dense_kernel<false>), grid, dim3(RNT), 0, s, a);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e =
+      launch_kernel(out_f32 ? attn_dense_kernel<true> : attn_dense_kernel<false>, grid, dim3(RNT), s, a);
   if (e != hipSuccess) return e;
   return launch_attn_merge(a, out_f32, s);
 }

@@ -3,7 +3,8 @@
 //
 // Quantisation (one work-group per tensor x (b, h) x 128-token block):
 //   absmax over the block (fp32), inv = 448 / absmax, s = absmax / 448,
-//   code = e4m3_rne(clamp(x * inv, +-448)) via v_cvt_pk_fp8_f32.
+//   code = e4m3_rne(clamp(x * inv, +-448)) via v_cvt_pk_fp8_f32; a block
+//   with absmax = 0 or 448 / absmax = inf gets s = 1 and zero codes.
 //   Q and K codes are stored row-major [BH][Np][128]; V codes transposed
 //   [BH][128][Np] with every 64-key group's 4-key groups permuted into the
 //   order the PV operand reads them, so the attention kernel copies tiles
@@ -102,8 +103,12 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(Fp8Args a) {
   if (lane == 0) red[wave] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float inv = (amax > 0.f) ? 448.0f / amax : 0.f;
-  if (tid == 0) scales[(int64_t)bh * a.nb + kb] = (amax > 0.f) ? amax / 448.0f : 1.0f;
+  // A block whose absmax is 0, or so small that 448 / absmax is not a finite
+  // fp32 number (absmax below 448 / FLT_MAX, about 1.3e-36), is stored as a
+  // zero block: scale 1 and all codes 0 (+0), whatever the signs of its zeros.
+  const float inv = 448.0f / amax;
+  const bool zero_block = !(inv <= 3.40282347e38f);
+  if (tid == 0) scales[(int64_t)bh * a.nb + kb] = zero_block ? 1.0f : amax / 448.0f;
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(Fp8Args a) {
           y[2 * e] = fminf(fmaxf(bf16_lo(w) * inv, -448.f), 448.f);
           y[2 * e + 1] = fminf(fmaxf(bf16_hi(w) * inv, -448.f), 448.f);
         }
-        codes[r][hf] = cvt4_e4m3(y[0], y[1], y[2], y[3]);
+        codes[r][hf] = zero_block ? 0u : cvt4_e4m3(y[0], y[1], y[2], y[3]);
       }
     if (!is_v) {
       uint8_t* dst = (tensor == 0 ? a.q8 : a.k8) + ((int64_t)bh * a.np + kb * kBlock + 4 * kg[i]) * D + 8 * cc[i];
@@ -491,8 +496,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
 hipError_t launch_fp8_quantize(const Fp8Args& a, hipStream_t s) {
   const int64_t nwg = 3LL * a.B * a.H * a.nb;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(fp8_quantize_kernel, dim3((unsigned)nwg), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(fp8_quantize_kernel, dim3((unsigned)nwg), dim3(256), s, a);
 }
 
 hipError_t launch_attn_fp8(const Fp8Args& args, bool out_f32, hipStream_t s) {
@@ -509,9 +513,8 @@ hipError_t launch_attn_fp8(const Fp8Args& args, bool out_f32, hipStream_t s) {
     a.ntail = 0;
     a.split = 1;
   }
-  if (out_f32) hipLaunchKernelGGL((attn_fp8_kernel<8, true>), dim3((unsigned)nwg), dim3(512), 0, s, a, nqb);
-  else hipLaunchKernelGGL((attn_fp8_kernel<8, false>), dim3((unsigned)nwg), dim3(512), 0, s, a, nqb);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = launch_kernel(out_f32 ? attn_fp8_kernel<8, true> : attn_fp8_kernel<8, false>,
+                                     dim3((unsigned)nwg), dim3(512), s, a, nqb);
   if (e != hipSuccess || !split) return e;
   // Merge the split key ranges (the weights are in units of 1/448).
   AttnArgs m = {};

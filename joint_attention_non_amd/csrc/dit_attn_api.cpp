@@ -281,15 +281,29 @@ int dit_attn_fwd_ws(const dit_attn_shape* shape, const void* q, const void* k, c
                     "dit_attn_fwd_ws launch");
 }
 
+size_t dit_attn_fwd_blocksparse_workspace_bytes(const dit_attn_shape* shape) {
+  (void)shape;
+  return 0;   // the block-sparse kernel keeps no cross-work-group state
+}
+
 int dit_attn_fwd_blocksparse(const dit_attn_shape* shape, const void* q, const void* k, const void* v, void* o,
                              float* lse, const uint8_t* block_mask, int64_t mask_stride_bh, int32_t block_size,
-                             void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = '\0';
   int rc = check_common(shape, q, k, v, o, lse);
   if (rc) return rc;
   if (block_mask == nullptr) return fail(DIT_ATTN_ERR_INVALID_ARG, "block_mask is NULL");
   if (block_size != 128) return fail(DIT_ATTN_ERR_UNSUPPORTED, "block_size=%d: only 128 is built", block_size);
   if (mask_stride_bh < 0) return fail(DIT_ATTN_ERR_INVALID_ARG, "mask_stride_bh is negative");
+  const size_t need = dit_attn_fwd_blocksparse_workspace_bytes(shape);
+  if (need > 0) {
+    if (workspace == nullptr) return fail(DIT_ATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (!aligned(workspace, 256)) return fail(DIT_ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(DIT_ATTN_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, need);
+  } else if (workspace != nullptr && !aligned(workspace, 256)) {
+    return fail(DIT_ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
   dit::AttnArgs a;
   fill_common(shape, q, k, v, o, lse, a);
   a.mask = block_mask;

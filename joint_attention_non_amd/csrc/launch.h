@@ -63,6 +63,15 @@ struct Fp8Args {
   float* part;          // [ntail * split][bm rows][kPartRow] fp32
 };
 
+// Launch `kernel` and return the status of this launch alone: hipLaunchKernel
+// reports it directly, whereas hipGetLastError would also return (and clear)
+// an error left on the thread by an earlier, unrelated HIP call.
+template <typename... P>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, const P&... args) {
+  void* argv[] = {const_cast<void*>(static_cast<const void*>(&args))...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, s);
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a, bool out_f32, bool sparse, hipStream_t s);
 hipError_t launch_attn_merge(const AttnArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_fp8_quantize(const Fp8Args& a, hipStream_t s);

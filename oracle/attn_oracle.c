@@ -170,7 +170,10 @@ uint8_t oracle_e4m3_encode(double x)
  *   inv    = 448 / absmax                                      (fp32 divide)
  *   code   = e4m3(clamp(x * inv, -448, 448))                   (fp32 multiply)
  *   scale  = absmax / 448                                      (fp32 divide)
- * absmax == 0 gives scale 1 and all-zero codes.  The quantised code is an
+ * absmax == 0, or an absmax so small that the fp32 quotient 448 / absmax
+ * overflows to infinity, gives scale 1 and all-zero codes (+0): there is no
+ * finite fp32 scale that maps such a block onto the e4m3 range, and its
+ * values (below 1.3e-36) are zero to every tolerance used.  The quantised code is an
  * integer decided by floating point, so it is decided in fp32, the precision
  * the device quantiser uses.
  * x: [BH][N][D] fp32 (bf16 values), codes: [BH][N][D], scales: [BH][nb]. */
@@ -190,12 +193,14 @@ void oracle_fp8_quantize(int64_t BH, int64_t N, int64_t D, int64_t block,
                 const float a = fabsf(xb[j * D + d]);
                 if (a > amax) amax = a;
             }
-        if (amax == 0.0f) {
+        const float inv = 448.0f / amax;
+        if (amax == 0.0f || isinf(inv)) {
+            /* nothing to scale: an all-zero block, or one so small that
+             * 448 / absmax overflows fp32 (absmax < 448 / FLT_MAX) */
             scales[t] = 1.0f;
             for (int64_t j = j0; j < j1; ++j) memset(cb + j * D, 0, (size_t)D);
             continue;
         }
-        const float inv = 448.0f / amax;
         scales[t] = amax / 448.0f;
         for (int64_t j = j0; j < j1; ++j)
             for (int64_t d = 0; d < D; ++d) {

@@ -6,6 +6,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import joint_attention_non_amd as dit
 
@@ -25,7 +26,8 @@ def test_header_declares_the_expected_calls():
     names = _declared()
     for n in ("dit_attn_fwd", "dit_attn_fwd_ws", "dit_attn_fwd_workspace_bytes",
               "dit_attn_fwd_fp8", "dit_attn_fwd_fp8_workspace_bytes",
-              "dit_attn_fp8_quantize", "dit_attn_fwd_blocksparse", "dit_attn_status_string",
+              "dit_attn_fp8_quantize", "dit_attn_fwd_blocksparse",
+              "dit_attn_fwd_blocksparse_workspace_bytes", "dit_attn_status_string",
               "dit_attn_last_error", "dit_attn_version"):
         assert n in names
 
@@ -92,9 +94,80 @@ def test_blocksparse_rejects_bad_mask_arguments():
     lib = dit.load()
     s = _shape()
     f = lib.dit_attn_fwd_blocksparse
-    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, None, 0, 128, None) == INVALID
-    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, 64, None) == UNSUPPORTED
-    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, -1, 128, None) == INVALID
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, None, 0, 128, None, 0, None) == INVALID
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, 64, None, 0, None) == UNSUPPORTED
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, -1, 128, None, 0, None) == INVALID
+    # the workspace this build needs is none; a misaligned one is still refused
+    assert lib.dit_attn_fwd_blocksparse_workspace_bytes(ctypes.byref(s)) == 0
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, 128, FAKE + 16, 64, None) == WORKSPACE
+
+
+class _DeviceLike(torch.Tensor):
+    """A host tensor that reports itself as a device tensor, so the binding's
+    argument checks (which all run before any library call) can be exercised
+    without a GPU."""
+
+    @property
+    def is_cuda(self):
+        return True
+
+
+def _dev(t):
+    return t.as_subclass(_DeviceLike)
+
+
+def _qkv(B=1, H=2, N=300):
+    q = _dev(torch.zeros((B, H, N, 128), dtype=torch.bfloat16))
+    return q, q, q
+
+
+@pytest.mark.parametrize("make_out,msg", [
+    (lambda: torch.zeros((1, 2, 300, 128), dtype=torch.bfloat16), "device tensor"),       # host tensor
+    (lambda: _dev(torch.zeros((1, 2, 300, 128), dtype=torch.float32)), "bfloat16"),       # wrong dtype
+    (lambda: _dev(torch.zeros((1, 2, 299, 128), dtype=torch.bfloat16)), "shape"),         # too short
+    (lambda: _dev(torch.zeros((1, 2, 128, 300), dtype=torch.bfloat16)).transpose(2, 3), "contiguous"),
+])
+def test_binding_rejects_bad_out(make_out, msg):
+    q, k, v = _qkv()
+    with pytest.raises(ValueError, match=msg):
+        dit.attn_fwd(q, k, v, out=make_out())
+
+
+def test_binding_rejects_fp32_flag_with_bf16_out_and_bad_lse_out():
+    q, k, v = _qkv()
+    with pytest.raises(ValueError, match="float32"):
+        dit.attn_fwd(q, k, v, out_fp32=True, out=_dev(torch.zeros((1, 2, 300, 128), dtype=torch.bfloat16)))
+    with pytest.raises(ValueError, match="lse_out"):
+        dit.attn_fwd(q, k, v, lse_out=_dev(torch.zeros((1, 2, 299), dtype=torch.float32)))
+    with pytest.raises(ValueError, match="lse_out"):
+        dit.attn_fwd_fp8(q, k, v, lse_out=_dev(torch.zeros((1, 2, 300), dtype=torch.float64)))
+
+
+def test_binding_rejects_bad_workspace():
+    q, k, v = _qkv()
+    for ws in (torch.zeros(4096, dtype=torch.uint8),                 # host memory
+               _dev(torch.zeros(1024, dtype=torch.float32)),         # not bytes
+               _dev(torch.zeros((2, 4096), dtype=torch.uint8))[:, ::2]):   # not contiguous
+        with pytest.raises(ValueError, match="workspace"):
+            dit.attn_fwd(q, k, v, workspace=ws)
+        with pytest.raises(ValueError, match="workspace"):
+            dit.attn_fwd_fp8(q, k, v, workspace=ws)
+
+
+@pytest.mark.parametrize("shape", [(2, 3), (3, 2), (3, 3, 3), (1, 3, 3), (2, 1, 3, 3), (4, 4)])
+def test_binding_rejects_masks_that_do_not_cover_every_slice(shape):
+    """N = 300 gives nb = 3; B*H = 2.  A short mask, one built for another N,
+    or a [1, nb, nb] mask used with two heads would be read past its end."""
+    q, k, v = _qkv()
+    mask = _dev(torch.ones(shape, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="block_mask"):
+        dit.attn_fwd_blocksparse(q, k, v, mask)
+
+
+def test_binding_mask_strides():
+    q, _, _ = _qkv(B=1, H=2, N=300)
+    for shape, stride in (((3, 3), 0), ((2, 3, 3), 9), ((1, 2, 3, 3), 9)):
+        assert dit._mask_stride(_dev(torch.ones(shape, dtype=torch.uint8)), q, 128) == stride
 
 
 def test_fp8_workspace_size_and_checks():

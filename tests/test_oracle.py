@@ -376,3 +376,100 @@ def test_fp8_recipe_error_band_vs_unquantised_oracle():
     assert 0.02 <= rel <= 0.09, rel
     assert cos >= 0.99
     assert abs(np.mean(a - b)) <= 0.05 * np.sqrt(np.mean((a - b) ** 2))
+
+
+def _torch_dec(codes):
+    """e4m3 codes -> float64 through torch's own float8_e4m3fn decoder."""
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_e4m3(x32):
+    """float32 values in [0, 448] -> e4m3 codes by torch's cast (RNE)."""
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def _recipe_rows_numpy(q8, k8, v8, sq, sk, sv, scale, i, final_max=False, block=128):
+    """Row i of (0, 0) of the fp8 recipe restated with numpy, torch's e4m3
+    codec and no shared code: key blocks in order; each block's P8 is rounded
+    against the running max m_kb (or, for the negative control, against the
+    row's final max); accumulator and row sum carried with exp(m_old - m_new)."""
+    N = q8.shape[2]
+    nb = (N + block - 1) // block
+    qd = _torch_dec(q8[0, 0, i])
+    kd, vd = _torch_dec(k8[0, 0]), _torch_dec(v8[0, 0])
+    qb = i // block
+    t = np.concatenate([scale * float(sq[0, 0, qb]) * float(sk[0, 0, kb]) *
+                        (kd[kb * block:(kb + 1) * block] @ qd) for kb in range(nb)])
+    m_final = t.max()
+    m, l, acc, ms = -np.inf, 0.0, np.zeros(q8.shape[3]), []
+    for kb in range(nb):
+        tb = t[kb * block:(kb + 1) * block]
+        mnew = max(m, tb.max())
+        alpha = 0.0 if m == -np.inf else math.exp(m - mnew)
+        ref = m_final if final_max else mnew
+        w = np.exp(tb - ref)
+        p = _torch_dec(_torch_e4m3(w.astype(np.float32) * np.float32(448.0))) / 448.0
+        if final_max:
+            l += p.sum()
+            acc += float(sv[0, 0, kb]) * (p @ vd[kb * block:(kb + 1) * block])
+        else:
+            l = alpha * l + p.sum()
+            acc = alpha * acc + float(sv[0, 0, kb]) * (p @ vd[kb * block:(kb + 1) * block])
+        m = mnew
+        ms.append(mnew)
+    return acc / l, ms
+
+
+@pytest.mark.parametrize("N,gaps", [(256, (2.3,)), (384, (1.7, 3.1))])
+def test_fp8_recipe_running_max_across_key_blocks(N, gaps):
+    """The running max moves between key blocks: block b (b >= 1) holds one
+    key whose logit is gaps[b-1] above every earlier logit of the row, so
+    each block's weights are rounded to e4m3 against a different max.  The
+    oracle must equal a numpy / torch-codec restatement of that schedule, and
+    must differ clearly from the variant that rounds every block against the
+    row's final max (a plausible mistake no other pin catches)."""
+    q, k, v = make_qkv(1, 1, N, 128, seed=19)
+    i = 5
+    scale = 1.0 / math.sqrt(128)
+    qi = q[0, 0, i].double()
+    base = float((k[0, 0, :128].double() @ qi).max()) * scale
+    for b, gap in enumerate(gaps, start=1):
+        target = base + sum(gaps[:b])          # logit of the planted key of block b
+        k[0, 0, 128 * b + 7] = (target / (scale * float(qi @ qi)) * qi).to(torch.bfloat16)
+    q8, sq = oracle.fp8_quantize(q)
+    k8, sk = oracle.fp8_quantize(k)
+    v8, sv = oracle.fp8_quantize(v)
+    o, _ = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale, rows=np.array([i]))
+    ref, ms = _recipe_rows_numpy(q8, k8, v8, sq, sk, sv, scale, i)
+    wrong, _ = _recipe_rows_numpy(q8, k8, v8, sq, sk, sv, scale, i, final_max=True)
+    # the set-up really moves the max at every block boundary
+    assert all(b - a > 1.0 for a, b in zip(ms, ms[1:])), ms
+    assert np.max(np.abs(o[0] - ref)) <= 1e-12
+    assert np.max(np.abs(o[0] - wrong)) >= 1e-4
+
+
+def test_fp8_quantize_tiny_block_is_a_zero_block():
+    """448 / absmax overflows fp32 for absmax below 448 / FLT_MAX (~1.3e-36):
+    such a block is stored like an all-zero one (scale 1, codes +0), also when
+    it holds negative zeros; just above the bound it is quantised normally
+    (absmax lands on code 448)."""
+    x = torch.zeros((1, 3, 384, 128), dtype=torch.float32)
+    g = torch.Generator().manual_seed(20)
+    x[0, 0, 0:128] = torch.randn((128, 128), generator=g) * 1e-37    # absmax ~4e-37
+    x[0, 0, 128:256] = -0.0
+    x[0, 0, 256:384] = torch.randn((128, 128), generator=g)
+    big = 4.0 * 448.0 / float(np.finfo(np.float32).max)                 # absmax above the bound
+    x[0, 1, 0:128] = torch.randn((128, 128), generator=g) * (big / 4.0)
+    x[0, 1, 0, 0] = big
+    xb = x.to(torch.bfloat16)
+    amax0 = np.float32(xb[0, 0, :128].float().abs().max())
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(448.0) / amax0)            # the block really is below the bound
+    codes, scales = oracle.fp8_quantize(xb)
+    assert scales[0, 0, 0] == 1.0 and np.all(codes[0, 0, 0:128] == 0)
+    assert scales[0, 0, 1] == 1.0 and np.all(codes[0, 0, 128:256] == 0)
+    amax1 = np.float32(xb[0, 1, :128].float().abs().max())
+    assert np.isfinite(np.float32(448.0) / amax1)
+    assert scales[0, 1, 0] == amax1 / np.float32(448.0)
+    assert np.max(np.abs(oracle.e4m3_decode_array(codes[0, 1, :128]))) == 448.0
