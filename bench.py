@@ -12,13 +12,17 @@ already resident in HBM).  `value` is the algorithmic TFLOP/s of that step
 (dit_attn_fwd) is timed beside it as `ms_no_split`.
 
 In the same run and on the same stream, timed the same way (W warm-ups, then
-K timed launches between HIP events), the other kernels of the path are
-reported as legs: the fp8 recipe (quantisation pass + fp8 attention) and the
-block-sparse kernel at the same 2048^2 shape with B=1 (optionally the dense
-kernel at the 1024^2 and image-to-image shapes).  For the step, launch_stats
-adds per-launch min / median times and one cold-cache launch.  The fp64 CPU
-oracle is timed on a bounded sample of rows of the same workload as the CPU
-baseline.
+K timed launches between HIP events), the other configurations are reported
+as legs: the fp8 recipe (quantisation pass + fp8 attention) and the
+block-sparse kernel at the 2048^2 shape with B=1, the dense kernel at the
+1024^2 shape and on the image-to-image joint sequence, and the tiny shape
+(launch-bound: its time per launch comes from a HIP graph of many launches,
+so host-side call overhead is not counted).  For the step, launch_stats adds
+per-launch min / median times and one cold-cache launch.  The fp64 CPU
+oracle is timed on a bounded sample of rows of the headline workload (the
+CPU baseline); the same leg checks the fp8 leg's output against the oracle
+on rows of every work-group (cosine and relative L2 against the exact
+attention and against the oracle's fp8 recipe), outside every timed region.
 
 Prints ONE JSON line.
 """
@@ -134,6 +138,54 @@ def _cpu_baseline(w, q, k, v, budget_s=18.0):
                       f"fp64, {dt:.1f} s"}
 
 
+def _graph_us_per_launch(call, n, torch):
+    """GPU time per launch of call() from a HIP graph holding n launches."""
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * n)
+
+
+def _fp8_accuracy(wf, rows, got):
+    """Part of the oracle leg: the fp8 output on `rows` (first, last and one
+    random row of every 256-row work-group) against the oracle's exact
+    attention on the unquantised inputs and against its fp8 recipe."""
+    import numpy as np
+    import oracle
+    from workloads import make_workload_inputs
+    q, k, v, _ = make_workload_inputs(wf, seed=0)
+    ref, _ = oracle.attn(q, k, v, wf.scale, rows=rows)
+    q8, sq = oracle.fp8_quantize(q)
+    k8, sk = oracle.fp8_quantize(k)
+    v8, sv = oracle.fp8_quantize(v)
+    rec, _ = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, wf.scale, rows=rows)
+    a = got.double().numpy().ravel()
+
+    def cmp(b):
+        b = b.ravel()
+        return {"cos": round(float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b))), 6),
+                "rel_l2": round(float(np.linalg.norm(a - b) / np.linalg.norm(b)), 5)}
+    e_ref, e_rec = cmp(ref), cmp(rec)
+    rr = rec.ravel()
+    b = ref.ravel()
+    return {"rows": int(rows.numel()), "vs_exact": e_ref, "vs_recipe": e_rec,
+            "recipe_vs_exact_rel_l2": round(float(np.linalg.norm(rr - b) / np.linalg.norm(b)), 5),
+            "gate": {"cos_min": 0.99, "rel_l2_max": 0.05,
+                     "cos_met": e_ref["cos"] >= 0.99, "rel_l2_met": e_ref["rel_l2"] <= 0.05}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,16 +193,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--legs", default="all", choices=["all", "none"],
-                    help="also time the fp8 and block-sparse kernels at the 2048^2 shape")
+                    help="also time the fp8, block-sparse, 1024^2, image-to-image and tiny legs")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one device-to-device copy of MIB MiB (a kernel of "
                          "known traffic, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--i2i", action="store_true",
-                    help="also time the dense kernel on the image-to-image joint sequence "
-                         "(512 text + 16384 target + 16384 reference tokens, B=2)")
-    ap.add_argument("--img1024", action="store_true",
-                    help="also time the dense kernel at the 1024^2 shape (same kernel name as "
-                         "the headline, so keep it out of profiled runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -161,7 +207,7 @@ def main():
     import torch
 
     import joint_attention_non_amd as dit
-    from workloads import WORKLOADS, make_workload_inputs
+    from workloads import WORKLOADS, block_rows, make_workload_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -199,6 +245,7 @@ def main():
     del o, wsb
 
     legs = {}
+    fp8_inputs = None
     if args.legs == "all":
         # fp8 recipe at 2048^2, B=1
         wf = WORKLOADS["img2048_fp8"]
@@ -212,6 +259,9 @@ def main():
         ms_q = _time_launches(lambda: dit.fp8_quantize(qf, kf, vf, workspace=ws),
                               args.steps, args.warmup, torch)
         ms_a = ms_f - ms_q
+        fp8_rows = block_rows(wf.batch, wf.heads, wf.seqlen, 256, seed=5)
+        fp8_out = of.reshape(-1, wf.head_dim)[fp8_rows.to(dev)].float().cpu()
+        fp8_inputs = (wf, fp8_rows, fp8_out)
         ff = _flops_dense(wf.batch, wf.heads, wf.seqlen, wf.head_dim)
         nbq = (wf.seqlen + 127) // 128
         qbytes = (3 * qf.numel() * 2                                  # bf16 Q, K, V read
@@ -250,23 +300,42 @@ def main():
         log(f"[bench] {wsp.name}: {legs[wsp.name]}")
         del qs, ks, vs, md, os_
 
-    for flag, wname in ((args.i2i, "i2i2048"), (args.img1024, "img1024")):
-        if not flag:
-            continue
-        w1 = WORKLOADS[wname]
-        log(f"[bench] leg {w1.name}")
-        q1, k1, v1, _ = make_workload_inputs(w1, seed=0)
-        q1, k1, v1 = (t.to(dev) for t in (q1, k1, v1))
-        o1 = torch.empty_like(q1)
-        ws1 = dit.fwd_workspace(q1)
-        ms_1 = _time_launches(lambda: dit.attn_fwd(q1, k1, v1, out=o1, workspace=ws1),
-                              max(args.steps, 50) if w1.seqlen < 8192 else args.steps,
-                              args.warmup, torch)
-        f1 = _flops_dense(w1.batch, w1.heads, w1.seqlen, w1.head_dim)
-        legs[w1.name] = {"ms": round(ms_1, 4), "achieved": round(f1 / (ms_1 * 1e-3) / 1e12, 2),
-                         "unit": "TFLOP/s", "frac": round(f1 / (ms_1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        log(f"[bench] {w1.name}: {legs[w1.name]}")
-        del q1, k1, v1, o1, ws1
+        for wname in ("img1024", "i2i2048"):
+            w1 = WORKLOADS[wname]
+            log(f"[bench] leg {w1.name}")
+            q1, k1, v1, _ = make_workload_inputs(w1, seed=0)
+            q1, k1, v1 = (t.to(dev) for t in (q1, k1, v1))
+            o1 = torch.empty_like(q1)
+            ws1 = dit.fwd_workspace(q1)
+            ms_1 = _time_launches(lambda: dit.attn_fwd(q1, k1, v1, out=o1, workspace=ws1),
+                                  max(args.steps, 50) if w1.seqlen < 8192 else args.steps,
+                                  args.warmup, torch)
+            f1 = _flops_dense(w1.batch, w1.heads, w1.seqlen, w1.head_dim)
+            legs[w1.name] = {"ms": round(ms_1, 4), "achieved": round(f1 / (ms_1 * 1e-3) / 1e12, 2),
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(f1 / (ms_1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                             "shape": f"B{w1.batch} H{w1.heads} N{w1.seqlen}"}
+            log(f"[bench] {w1.name}: {legs[w1.name]}")
+            del q1, k1, v1, o1, ws1
+
+        # the tiny shape is launch-bound: time a graph of many launches
+        wt = WORKLOADS["tiny"]
+        log(f"[bench] leg {wt.name}")
+        qt, kt, vt, _ = make_workload_inputs(wt, seed=0)
+        qt, kt, vt = (t.to(dev) for t in (qt, kt, vt))
+        ot = torch.empty_like(qt)
+        wst = dit.fwd_workspace(qt)
+        tiny = {}
+        for label, call in (("us_per_launch", lambda: dit.attn_fwd(qt, kt, vt, out=ot, workspace=wst)),
+                            ("us_per_launch_no_split", lambda: dit.attn_fwd(qt, kt, vt, out=ot))):
+            tiny[label] = round(_graph_us_per_launch(call, 200, torch), 2)
+        ft = _flops_dense(wt.batch, wt.heads, wt.seqlen, wt.head_dim)
+        tiny["achieved_tflops"] = round(ft / (tiny["us_per_launch"] * 1e-6) / 1e12, 3)
+        tiny["timing"] = "HIP graph of 200 back-to-back launches, replayed; graph time / 200"
+        tiny["shape"] = f"B{wt.batch} H{wt.heads} N{wt.seqlen}"
+        legs[wt.name] = tiny
+        log(f"[bench] {wt.name}: {tiny}")
+        del qt, kt, vt, ot, wst
 
     if args.calib_copy:
         n = args.calib_copy * (1 << 20) // 4
@@ -283,6 +352,10 @@ def main():
         log("[bench] CPU oracle baseline (bounded sample)")
         cpu = _cpu_baseline(w, q, k, v)
         log(f"[bench] cpu: {cpu}")
+        if fp8_inputs is not None:
+            log("[bench] fp8 accuracy against the oracle (rows of every work-group)")
+            legs["img2048_fp8"]["accuracy"] = _fp8_accuracy(*fp8_inputs)
+            log(f"[bench] fp8 accuracy: {legs['img2048_fp8']['accuracy']}")
 
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,

@@ -13,7 +13,8 @@ import joint_attention_non_amd as dit
 import oracle
 from tests._metrics import (BF16_MAX_ABS, BF16_MEAN_ABS, LSE_ABS, bf16_elementwise_ok, errors,
                             rne_bf16, to64)
-from workloads import WORKLOADS, make_qkv, make_workload_inputs, sample_rows
+from tests._rows import block_rows, nan_like_out, nan_lse
+from workloads import WORKLOADS, make_qkv, make_workload_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -125,20 +126,35 @@ def test_constant_v():
     assert float((o - 0.75).abs().max()) <= 1e-3
 
 
-def _sampled_parity(name, n_rows):
+def _blockwise_parity(name, workspace: bool):
+    """Every 384-row work-group of the launch is checked: its first, last and
+    one random row against the oracle, after the outputs were pre-filled with
+    NaN (a work-group that never stores its rows would leave NaN behind).
+    With `workspace`, the launch is the one the benchmark times
+    (dit_attn_fwd_ws: the last partial round split over key ranges, the
+    workspace also pre-filled with NaN)."""
     w = WORKLOADS[name]
-    _say(f"case: {w.describe()} sampled rows={n_rows}")
+    B, H, N = w.batch, w.heads, w.seqlen
+    _say(f"case: {w.describe()} blockwise, workspace={workspace}")
     q, k, v, _ = make_workload_inputs(w, seed=0)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
-    o16, o32, lse = _run_both(qd, kd, vd)
+    ws = None
+    if workspace:
+        ws = dit.fwd_workspace(qd)
+        ws.view(torch.uint8).fill_(0xFF)
+    o32 = dit.attn_fwd(qd, kd, vd, out_fp32=True, out=nan_like_out(B, H, N, True, DEV), workspace=ws)
+    o16, lse = dit.attn_fwd(qd, kd, vd, return_lse=True, out=nan_like_out(B, H, N, False, DEV),
+                            lse_out=nan_lse(B, H, N, DEV), workspace=ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o32).all()) and bool(torch.isfinite(o16).all())
+    assert bool(torch.isfinite(lse).all())
     assert torch.equal(rne_bf16(o32).view(torch.int16), o16.view(torch.int16))
-    assert bool(torch.isfinite(o32).all())
-    rows = sample_rows(w.batch, w.heads, w.seqlen, n_rows, seed=0)
+    rows = block_rows(B, H, N, 384, seed=0)
     ref, ref_lse = oracle.attn(q, k, v, w.scale, rows=rows)
     o32r = o32.reshape(-1, 128)[rows.to(DEV)].cpu()
     o16r = o16.reshape(-1, 128)[rows.to(DEV)].cpu()
     e32, e16 = errors(o32r, ref), errors(o16r, ref)
-    _say(f"fp32-out {e32}  bf16-out {e16}")
+    _say(f"rows={rows.numel()} fp32-out {e32}  bf16-out {e16}")
     assert e32["max_abs"] <= BF16_MAX_ABS and e32["mean_abs"] <= BF16_MEAN_ABS, e32
     assert bf16_elementwise_ok(o16r, ref).all()
     assert e16["mean_abs"] <= BF16_MEAN_ABS
@@ -146,17 +162,97 @@ def _sampled_parity(name, n_rows):
     assert np.max(np.abs(lse_r - ref_lse)) <= LSE_ABS
 
 
-def test_img1024_sampled_parity():
-    _sampled_parity("img1024", 512)
+def test_img1024_full_parity():
+    """Every one of the 110,592 output rows of the 1024^2 shape."""
+    w = WORKLOADS["img1024"]
+    B, H, N = w.batch, w.heads, w.seqlen
+    _say(f"case: {w.describe()} all rows")
+    q, k, v, _ = make_workload_inputs(w, seed=0)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    ws = dit.fwd_workspace(qd)
+    for wsp in (None, ws):
+        o32 = dit.attn_fwd(qd, kd, vd, out_fp32=True, out=nan_like_out(B, H, N, True, DEV), workspace=wsp)
+        o16, lse = dit.attn_fwd(qd, kd, vd, return_lse=True, out=nan_like_out(B, H, N, False, DEV),
+                                lse_out=nan_lse(B, H, N, DEV), workspace=wsp)
+        torch.cuda.synchronize()
+        assert torch.equal(rne_bf16(o32).view(torch.int16), o16.view(torch.int16))
+        e32, e16 = _check_against(q, k, v, w.scale, o32, o16, lse)
+        _say(f"workspace={wsp is not None}: fp32-out {e32}  bf16-out {e16}")
 
 
-def test_img2048_cfg_pair_sampled_parity():
-    _sampled_parity("img2048", 384)
+def _check_against(q, k, v, scale, o32, o16, lse):
+    ref, ref_lse = oracle.attn(q, k, v, scale)
+    e32 = errors(o32, ref)
+    assert e32["max_abs"] <= BF16_MAX_ABS and e32["mean_abs"] <= BF16_MEAN_ABS, e32
+    assert bf16_elementwise_ok(o16, ref).all()
+    e16 = errors(o16, ref)
+    assert e16["mean_abs"] <= BF16_MEAN_ABS, e16
+    assert np.max(np.abs(to64(lse) - ref_lse)) <= LSE_ABS
+    return e32, e16
 
 
-def test_i2i2048_sampled_parity():
+@pytest.mark.parametrize("workspace", [False, True])
+def test_img2048_cfg_pair_blockwise_parity(workspace):
+    _blockwise_parity("img2048", workspace)
+
+
+@pytest.mark.parametrize("workspace", [False, True])
+def test_i2i2048_blockwise_parity(workspace):
     """Image-to-image joint sequence: text + target + reference latents."""
-    _sampled_parity("i2i2048", 256)
+    _blockwise_parity("i2i2048", workspace)
+
+
+# Rows whose logits ramp up over many 32-key tiles: the query row is a scaled
+# basis vector e_r, so key j's logit for it is (nearly) K[j, r], which is set
+# to slope * ln 2 * tile(j) for the tiles of the ramp -- a row max that grows
+# by `slope` log2 units per tile -- and falls back to N(0, 1) afterwards.
+# Slopes of 40 and 70 push a lane's weights past the 2^64 redo bound every
+# one or two tiles, 10 stays under it, 0 is flat; other rows of the same
+# waves see the ramps mixed into their own logits.
+RAMP_ROWS = [(0, 40.0), (17, 70.0), (47, 10.0), (48, 0.0), (130, 100.0), (301, 64.0), (777, 40.0)]
+
+
+def _ramp_inputs(N, seed, first_tile=1, last_tile=14, tile=32):
+    q, k, v = make_qkv(1, 1, N, 128, seed=seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    for r, (i, slope) in enumerate(RAMP_ROWS):
+        if i >= N:
+            continue
+        q[0, 0, i] = 0
+        q[0, 0, i, r] = math.sqrt(128.0)
+        for t in range(first_tile, last_tile + 1):
+            j0, j1 = t * tile, min(N, (t + 1) * tile)
+            if j0 >= N:
+                break
+            base = slope * math.log(2.0) * (t - first_tile + 1)
+            k[0, 0, j0:j1, r] = (base + 0.5 * torch.randn(j1 - j0, generator=g)).to(torch.bfloat16)
+    return q, k, v
+
+
+@pytest.mark.parametrize("N", [1000, 4000])
+def test_logit_ramp_over_many_tiles(N):
+    """The lazy reference max: the weights are taken against a reference that
+    may lag the row max, and the tile is redone (reference moved, O and l
+    rescaled) only when a lane's weight sum passes 2^64.  Full parity on rows
+    whose max climbs far beyond that bound over many tiles, for dit_attn_fwd,
+    dit_attn_fwd_ws (here a small grid, so every block is split over key
+    ranges and the partial results carry very different maxima into the
+    merge) and the block-sparse kernel with every block kept."""
+    _say(f"case: logit ramp N={N}")
+    q, k, v = _ramp_inputs(N, seed=26)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    scale = 1.0 / math.sqrt(128)
+    nb = (N + 127) // 128
+    ones = torch.ones((nb, nb), dtype=torch.uint8, device=DEV)
+    for label, fn in (("fwd", lambda **kw: dit.attn_fwd(qd, kd, vd, **kw)),
+                      ("fwd_ws", lambda **kw: dit.attn_fwd(qd, kd, vd, workspace=dit.fwd_workspace(qd), **kw)),
+                      ("sparse", lambda **kw: dit.attn_fwd_blocksparse(qd, kd, vd, ones, **kw))):
+        o32 = fn(out_fp32=True)
+        o16, lse = fn(return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(rne_bf16(o32).view(torch.int16), o16.view(torch.int16)), label
+        e32, e16 = _check_against(q, k, v, scale, o32, o16, lse)
+        _say(f"{label}: fp32-out {e32}")
 
 
 def test_long_sequence_sampled_parity():

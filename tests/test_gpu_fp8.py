@@ -10,7 +10,8 @@ import torch
 import joint_attention_non_amd as dit
 import oracle
 from tests._metrics import FP8_COS, FP8_REL_L2, FP8_RECIPE_REL_L2, errors, to64
-from workloads import WORKLOADS, make_qkv, make_workload_inputs, sample_rows
+from tests._rows import block_rows, nan_like_out, nan_lse
+from workloads import WORKLOADS, make_qkv, make_workload_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -136,23 +137,98 @@ def _split_rows(B, H, N):
     return torch.cat(rows), split
 
 
-def test_img2048_fp8_sampled_parity():
+def test_img2048_fp8_blockwise_parity():
+    """Every 256-row work-group: first, last and one random row of each block
+    of every head, outputs pre-filled with NaN and the workspace with 0xFF
+    bytes (an e4m3 NaN code and an fp32 NaN: every code, scale and partial
+    result the attention reads must have been written in the same call).  Rows of blocks outside the split
+    last round are gated against the oracle's recipe at 5e-3; rows of split
+    blocks as in test_img2048_fp8_split_rows."""
     w = WORKLOADS["img2048_fp8"]
-    _say(f"case: {w.describe()} sampled (rows outside split blocks)")
+    B, H, N = w.batch, w.heads, w.seqlen
+    _say(f"case: {w.describe()} blockwise")
     q, k, v, _ = make_workload_inputs(w, seed=0)
-    rows = sample_rows(w.batch, w.heads, w.seqlen, 256, seed=0)
-    split_rows, _ = _split_rows(w.batch, w.heads, w.seqlen)
-    rows = rows[~torch.isin(rows, split_rows)]
-    e_rec, e_ref, e_rr = _fp8_vs_oracles(q, k, v, rows=rows)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    ws = torch.full((dit.fp8_workspace_bytes(qd),), 0xFF, dtype=torch.uint8, device=DEV)
+    o32, lse = dit.attn_fwd_fp8(qd, kd, vd, out_fp32=True, return_lse=True, workspace=ws,
+                                out=nan_like_out(B, H, N, True, DEV), lse_out=nan_lse(B, H, N, DEV))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o32).all()) and bool(torch.isfinite(lse).all())
+    rows = block_rows(B, H, N, 256, seed=0)
+    split_rows, _ = _split_rows(B, H, N)
+    in_split = torch.isin(rows, split_rows)
+    q8, sq = oracle.fp8_quantize(q)
+    k8, sk = oracle.fp8_quantize(k)
+    v8, sv = oracle.fp8_quantize(v)
+    rec, _ = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, w.scale, rows=rows)
+    ref, _ = oracle.attn(q, k, v, w.scale, rows=rows)
+    got = o32.reshape(-1, 128)[rows.to(DEV)].cpu().double().numpy()
+    plain = (~in_split).numpy()
+    e_rec, e_ref, e_rr = errors(got[plain], rec[plain]), errors(got[plain], ref[plain]), \
+        errors(rec[plain], ref[plain])
+    _say(f"rows={int(plain.sum())} vs recipe {e_rec}  vs exact {e_ref}  recipe vs exact {e_rr}")
+    assert e_rec["rel_l2"] <= FP8_RECIPE_REL_L2, e_rec
+    assert e_ref["cos"] >= FP8_COS, e_ref
+    assert e_ref["rel_l2"] <= e_rr["rel_l2"] * 1.02 + 1e-3
+    sp = in_split.numpy()
+    if sp.any():
+        e_rec, e_ref, e_rr = errors(got[sp], rec[sp]), errors(got[sp], ref[sp]), errors(rec[sp], ref[sp])
+        _say(f"split rows={int(sp.sum())} vs recipe {e_rec}  vs exact {e_ref}  recipe vs exact {e_rr}")
+        assert e_ref["cos"] >= FP8_COS, e_ref
+        assert e_ref["rel_l2"] <= e_rr["rel_l2"] * 1.05 + 1e-3, (e_ref, e_rr)
+        assert e_rec["rel_l2"] <= 0.05, e_rec
+
+
+@pytest.mark.xfail(strict=True, reason="the e4m3 recipe itself (four e4m3-rounded operands) sits at relative "
+                                       "L2 of about 0.057 against the exact attention at this shape; the "
+                                       "kernel matches the recipe to 5e-3")
+def test_img2048_fp8_exact_attention_rel_l2_gate():
+    """The stated fp8 gate, relative L2 <= 5e-2 against the exact attention
+    on the unquantised inputs, on rows of every work-group.  Expected to
+    fail: see the xfail reason; cosine >= 0.99 holds."""
+    w = WORKLOADS["img2048_fp8"]
+    B, H, N = w.batch, w.heads, w.seqlen
+    q, k, v, _ = make_workload_inputs(w, seed=0)
+    rows = block_rows(B, H, N, 256, seed=1)
+    o = dit.attn_fwd_fp8(q.to(DEV), k.to(DEV), v.to(DEV), out_fp32=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle.attn(q, k, v, w.scale, rows=rows)
+    e = errors(o.reshape(-1, 128)[rows.to(DEV)].cpu(), ref)
+    _say(f"rows={rows.numel()} vs exact {e}")
+    assert e["cos"] >= FP8_COS
+    assert e["rel_l2"] <= FP8_REL_L2, e
+
+
+def _tiny_v_inputs(N=768, seed=65):
+    """V blocks of very different magnitudes between normal ones: absmax about
+    1e-30, 1e-35 (a V scale 1e33 times smaller than its neighbours') and
+    4e-37 (below 448 / FLT_MAX, stored as a zero block)."""
+    q, k, v = make_qkv(1, 2, N, 128, seed=seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    for blk, mag in ((1, 1e-30), (3, 1e-35), (4, 4e-37)):
+        x = torch.randn((2, 128, 128), generator=g)
+        v[0, :, blk * 128:(blk + 1) * 128] = (x / x.abs().amax() * mag).to(torch.bfloat16)
+    return q, k, v
+
+
+def test_quantizer_tiny_blocks_bit_exact():
+    _say("case: fp8 quantise tiny V blocks")
+    _check_quantizer(*_tiny_v_inputs())
+
+
+def test_fp8_tiny_v_blocks_parity():
+    """The attention carries its accumulator across key blocks whose V scales
+    differ by up to 1e33: the output stays finite and matches the recipe and
+    the exact attention like any other input."""
+    _say("case: fp8 attention with tiny V blocks")
+    q, k, v = _tiny_v_inputs()
+    o = dit.attn_fwd_fp8(q.to(DEV), k.to(DEV), v.to(DEV), out_fp32=True)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())
+    e_rec, e_ref, e_rr = _fp8_vs_oracles(q, k, v)
     _say(f"vs recipe {e_rec}  vs exact {e_ref}  recipe vs exact {e_rr}")
     assert e_rec["rel_l2"] <= FP8_RECIPE_REL_L2, e_rec
     assert e_ref["cos"] >= FP8_COS, e_ref
-    # The recipe itself sits near relL2 0.053 on N(0,1) inputs (four
-    # e4m3-rounded operands); report it, and require the kernel to add
-    # almost nothing to it.
-    assert e_ref["rel_l2"] <= e_rr["rel_l2"] * 1.02 + 1e-3
-    if e_ref["rel_l2"] > FP8_REL_L2:
-        _say(f"NOTE: relL2 {e_ref['rel_l2']:.4f} exceeds 5e-2; the recipe alone gives {e_rr['rel_l2']:.4f}")
 
 
 def test_img2048_fp8_split_rows():

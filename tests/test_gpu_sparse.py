@@ -10,7 +10,8 @@ import joint_attention_non_amd as dit
 import oracle
 from tests._metrics import (BF16_MAX_ABS, BF16_MEAN_ABS, LSE_ABS, bf16_elementwise_ok, errors,
                             rne_bf16, to64)
-from workloads import WORKLOADS, make_block_mask, make_qkv, make_workload_inputs, sample_rows
+from tests._rows import block_rows, nan_like_out, nan_lse
+from workloads import WORKLOADS, make_block_mask, make_qkv, make_workload_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -127,23 +128,29 @@ def test_per_head_masks():
     assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
 
 
-def test_img2048_sparse_sampled_parity():
+def test_img2048_sparse_blockwise_parity():
+    """Every 128-row work-group: first, last and one random row of each mask
+    block of every head against the oracle, outputs pre-filled with NaN."""
     w = WORKLOADS["img2048_sparse"]
-    _say(f"case: {w.describe()} sampled")
+    B, H, N = w.batch, w.heads, w.seqlen
+    _say(f"case: {w.describe()} blockwise")
     q, k, v, mask = make_workload_inputs(w, seed=0)
     _say(f"active blocks: {int(mask.sum())} of {mask.numel()}")
     qd, kd, vd, md = (t.to(DEV) for t in (q, k, v, mask))
-    o32 = dit.attn_fwd_blocksparse(qd, kd, vd, md, out_fp32=True)
-    o16 = dit.attn_fwd_blocksparse(qd, kd, vd, md)
+    o32 = dit.attn_fwd_blocksparse(qd, kd, vd, md, out_fp32=True, out=nan_like_out(B, H, N, True, DEV))
+    o16, lse = dit.attn_fwd_blocksparse(qd, kd, vd, md, return_lse=True, out=nan_like_out(B, H, N, False, DEV),
+                                        lse_out=nan_lse(B, H, N, DEV))
     torch.cuda.synchronize()
+    assert bool(torch.isfinite(o32).all()) and bool(torch.isfinite(lse).all())
     assert torch.equal(rne_bf16(o32).view(torch.int16), o16.view(torch.int16))
-    rows = sample_rows(w.batch, w.heads, w.seqlen, 384, seed=0)
-    ref, _ = oracle.attn(q, k, v, w.scale, mask=mask, rows=rows)
+    rows = block_rows(B, H, N, 128, seed=0)
+    ref, ref_lse = oracle.attn(q, k, v, w.scale, mask=mask, rows=rows)
     got = o32.reshape(-1, 128)[rows.to(DEV)].cpu()
     e = errors(got, ref)
-    _say(f"sparse fp32-out {e}")
+    _say(f"rows={rows.numel()} sparse fp32-out {e}")
     assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
     assert bf16_elementwise_ok(o16.reshape(-1, 128)[rows.to(DEV)].cpu(), ref).all()
+    assert np.max(np.abs(to64(lse.reshape(-1)[rows.to(DEV)].cpu()) - ref_lse)) <= LSE_ABS
 
 
 def test_long_sequence_sparse_sampled_parity():

@@ -147,3 +147,19 @@ def sample_rows(B: int, H: int, N: int, n: int, seed: int = 0) -> torch.Tensor:
                           total - 1 - (N % BLOCK)], dtype=torch.int64).clamp(0, total - 1)
     rows = torch.unique(torch.cat([fixed, picks]))
     return rows
+
+
+def block_rows(B: int, H: int, N: int, rows: int, seed: int = 0) -> torch.Tensor:
+    """Flat row ids (bh * N + i) that touch every block of `rows` query rows
+    of every (batch, head) slice: the block's first and last row and one
+    random row of it -- so a check on these rows sees every work-group of a
+    launch that gives one such block to each work-group."""
+    nqb = (N + rows - 1) // rows
+    g = torch.Generator().manual_seed(seed + 77)
+    lo = torch.arange(nqb) * rows
+    hi = torch.clamp(lo + rows, max=N) - 1
+    picks = []
+    for bh in range(B * H):
+        rnd = torch.minimum(lo + (torch.rand(nqb, generator=g) * rows).long(), hi)
+        picks.append(bh * N + torch.stack([lo, hi, rnd], 1).reshape(-1))
+    return torch.unique(torch.cat(picks))
