@@ -22,7 +22,9 @@
 //   l = alpha l + sum e4m3(y)        (row sum of the quantised weights, on
 //                                     the MFMA with an all-ones operand)
 //   A = A * alpha * sV_prev / sV + V8^T e4m3(y)^T
-// and at the end O = A * sV_last / l, lse = ln2 (m + log2(l / 448)).
+// and at the end O = A * sV_last / l, lse = ln2 (m + log2(l / 448)).  (A V
+// block whose scale is below 2^-64 of the largest one added so far is left
+// out of A, which keeps A finite whatever the spread of V scales; see VUnit.)
 #include "device_common.h"
 #include "launch.h"
 
@@ -292,11 +294,29 @@ __device__ __forceinline__ void pv8_tile(f32x16 (&oacc)[4], f32x16& lacc, const 
   }
 }
 
+// The PV accumulator A is carried in the dequantisation scale of the V block
+// last added to it (sv): moving to the next block's scale svt multiplies A by
+// sv / svt (with the softmax's alpha).  A V block whose scale is below 2^-64
+// times the largest scale added so far (vmax) is not added at all -- its
+// values are below 2^-64 of the largest V magnitude among the row's keys, so
+// leaving them out changes O by less than that -- while its weights still
+// count in the row sum: the row-sum MFMAs of that tile run at once and its
+// quantised weights are then zeroed, so the PV and row-sum MFMAs of the
+// pipeline add nothing for it.  That bounds the factor by 2^64 and A by about
+// 448^2 * keys * 2^64, far inside fp32, whatever the spread of V scales.  No
+// V block is left out of inputs whose V scales stay within 2^64 of each
+// other (every ordinary input).
+struct VUnit {
+  float sv;     // scale of the last V block added to A
+  float vmax;   // largest scale of the V blocks added to A
+};
+
 // Softmax of one tile (keys key0 ..): t = S f, new running max, quantised
 // weights e4m3(2^(t - m + log2 448)) into p8, and the running accumulator
-// and row sum brought to the new max and to this tile's V scale.
+// and row sum brought to the new max and to this tile's V scale (or the
+// tile's V left out, see VUnit).
 __device__ __forceinline__ void softmax8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f32x16& lacc, uint32_t (&p8)[2][8],
-                                         float& m_run, float& sv_prev, float f, float svt, float p_off, int key0,
+                                         float& m_run, VUnit& unit, float f, float svt, float p_off, int key0,
                                          int N, int h) {
   if (key0 + BN8 > N) {
     // Keys past N get -inf.  Element (kb, r) of this lane is key key0 + off
@@ -313,8 +333,12 @@ __device__ __forceinline__ void softmax8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f
         __builtin_amdgcn_sched_barrier(0);
       }
   }
-  const float vratio = sv_prev / svt;
-  sv_prev = svt;
+  const bool add_v = svt >= unit.vmax * 0x1p-64f;   // wave-uniform
+  const float vratio = add_v ? unit.sv / svt : 1.f;
+  if (add_v) {
+    unit.sv = svt;
+    unit.vmax = fmaxf(unit.vmax, svt);
+  }
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
@@ -344,6 +368,17 @@ __device__ __forceinline__ void softmax8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] *= g;
+  if (!add_v) {
+    // V block left out (see VUnit): count its weights now, then zero them.
+    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, p_frag8(p8, s), lacc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) p8[s][w] = 0u;
+    }
+  }
 }
 
 // Work-group: NW waves x 32 query rows.  Step t issues the QK^T MFMAs of
@@ -405,7 +440,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
 #pragma unroll
     for (int db = 0; db < 4; ++db) oacc[db][r] = 0.f;
   }
-  float m_run = -INFINITY, sv_prev = 1.f;
+  float m_run = -INFINITY;
+  VUnit unit = {svp[t0], svp[t0]};
 
   // ---- prologue: tiles t0 and t0+1 into LDS, t0+2 into registers ----
   Loader8<NT> ld;
@@ -419,7 +455,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
   f32x16 sacc[4];
   uint32_t p8[2][8];
   qk8_tile(sacc, smK[0], qf, l32, h);
-  softmax8(sacc, oacc, lacc, p8, m_run, sv_prev, fq * skp[t0], svp[t0], a.p_off, t0 * BN8, N, h);
+  softmax8(sacc, oacc, lacc, p8, m_run, unit, fq * skp[t0], svp[t0], a.p_off, t0 * BN8, N, h);
 
   int bc = 0;   // LDS buffer of tile t; tile t+1 is in bc+1, tile t+2 goes to bc+2 (mod 3)
   for (int t = t0; t + 1 < t1; ++t) {
@@ -439,7 +475,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre8, 0);
     step8_schedule<0>();
     __syncthreads();
-    softmax8(sacc, oacc, lacc, p8, m_run, sv_prev, fq * skp[t + 1], svp[t + 1], a.p_off, (t + 1) * BN8, N, h);
+    softmax8(sacc, oacc, lacc, p8, m_run, unit, fq * skp[t + 1], svp[t + 1], a.p_off, (t + 1) * BN8, N, h);
     bc = bn;
   }
   pv8_tile(oacc, lacc, p8, smV[bc], l32, h);
@@ -447,7 +483,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
   // ---- epilogue: O = A * sV_last / l ----
   const int64_t ob = b * a.os[0] + hd * a.os[1];
   const float lt = lacc[0];
-  const float inv = lt > 0.f ? sv_prev / lt : 0.f;
+  const float inv = lt > 0.f ? unit.sv / lt : 0.f;
+  const float ounit = unit.sv;
   const int row = q0 + l32;
   if (part >= 0) {
     // Partial result of one key range: A * sV_last (unnormalised O), m, l.
@@ -457,8 +494,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 t4 = {oacc[db][4 * r4 + 0] * sv_prev, oacc[db][4 * r4 + 1] * sv_prev,
-                            oacc[db][4 * r4 + 2] * sv_prev, oacc[db][4 * r4 + 3] * sv_prev};
+          const f32x4 t4 = {oacc[db][4 * r4 + 0] * ounit, oacc[db][4 * r4 + 1] * ounit,
+                            oacc[db][4 * r4 + 2] * ounit, oacc[db][4 * r4 + 3] * ounit};
           *reinterpret_cast<f32x4*>(pr + db * 32 + r4 * 8 + h * 4) = t4;
         }
       if (h == 0) {
