@@ -110,6 +110,28 @@ int dit_attn_fwd_ws(const dit_attn_shape* shape,
                     void* o, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * attention as dit_attn_fwd_ws (same arguments and errors, same kernels, same
+ * split plan, bit-identical output), with the partial results of the split
+ * tail blocks kept in a device array the library itself holds instead of a
+ * caller workspace.  The array holds dit_attn_fwd_noalloc_scratch_bytes()
+ * bytes (64 MiB) on every GPU the library runs on, until the process ends;
+ * a shape whose split needs more (dit_attn_fwd_workspace_bytes(shape) above
+ * that: more than about 330 compute units) is refused with
+ * DIT_ATTN_ERR_WORKSPACE before anything is launched.  Nothing in the array
+ * needs to start at any value (every partial result is written before it is
+ * read, in the same call).  All calls on one GPU share its array: calls that
+ * may overlap on one GPU (several streams, several host threads) race and
+ * must be serialised by the caller.  The call allocates and frees nothing;
+ * its first call on a device looks up that device's copy of the array. */
+int dit_attn_fwd_noalloc(const dit_attn_shape* shape,
+                         const void* q, const void* k, const void* v,
+                         void* o, float* lse, void* stream);
+
+/* Size in bytes of the device array dit_attn_fwd_noalloc uses. */
+size_t dit_attn_fwd_noalloc_scratch_bytes(void);
+
 /* Workspace bytes dit_attn_fwd_fp8 / dit_attn_fp8_quantize need for `shape`
  * (0 if the shape is invalid).  Layout, with BH = B*H, nb = ceil(N/128),
  * Np = 128*nb, each region starting at a 256-byte boundary in this order:

@@ -25,7 +25,7 @@ import torch
 
 __all__ = ["attn_fwd", "attn_fwd_fp8", "attn_fwd_blocksparse", "fp8_quantize",
            "fp8_workspace_bytes", "fwd_workspace_bytes", "fwd_workspace",
-           "blocksparse_workspace_bytes", "DitAttnError",
+           "blocksparse_workspace_bytes", "attn_fwd_noalloc", "DitAttnError",
            "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +68,10 @@ def load():
         lib.dit_attn_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.dit_attn_fwd_ws.argtypes = [sp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.dit_attn_fwd_ws.restype = ctypes.c_int
+        lib.dit_attn_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+        lib.dit_attn_fwd_noalloc.restype = ctypes.c_int
+        lib.dit_attn_fwd_noalloc_scratch_bytes.argtypes = []
+        lib.dit_attn_fwd_noalloc_scratch_bytes.restype = ctypes.c_size_t
         lib.dit_attn_fwd_fp8_workspace_bytes.argtypes = [sp]
         lib.dit_attn_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
         lib.dit_attn_fwd_fp8.argtypes = [sp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -199,6 +203,17 @@ def attn_fwd(q, k, v, scale=None, return_lse=False, out_fp32=False, out=None, wo
         _check_workspace(workspace, q)
         _check(load().dit_attn_fwd_ws(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                       _ptr(workspace), workspace.numel(), _stream()), "dit_attn_fwd_ws")
+    return _ret(o, lse, return_lse)
+
+
+def attn_fwd_noalloc(q, k, v, scale=None, return_lse=False, out_fp32=False, out=None, lse_out=None):
+    """dit_attn_fwd_noalloc: dit_attn_fwd_ws with the library's own static
+    scratch instead of a workspace (allocates nothing when `out` -- and
+    `lse_out` if lse is wanted -- are given)."""
+    o, lse = _outputs(q, return_lse, out_fp32, out, lse_out)
+    s = _shape(q, k, v, o, scale, FLAG_OUT_F32 if out_fp32 else 0)
+    _check(load().dit_attn_fwd_noalloc(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       _stream()), "dit_attn_fwd_noalloc")
     return _ret(o, lse, return_lse)
 
 

@@ -9,9 +9,18 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dit_attn.h"
 #include "launch.h"
+
+// Scratch of dit_attn_fwd_noalloc: the partial results of the split tail
+// blocks (see dit_attn_fwd_ws), in a device array the library owns, so that
+// the entry point allocates nothing.  Host code must never take this name's
+// address for device use: the device address of each GPU's copy comes from
+// hipGetSymbolAddress (scratch_device_ptr below).
+static constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -150,6 +159,28 @@ TailPlan tail_plan(const dit_attn_shape* sh, int cus, int rows, int tile_keys, b
   return t;
 }
 
+// Device address of `scratch` on the current device.  Each GPU holds its own
+// copy of the array; its address is looked up once per device, with that
+// device current, and kept.
+int scratch_device_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DIT_ATTN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(DIT_ATTN_ERR_UNSUPPORTED, "device %d: at most 64 devices", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(DIT_ATTN_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return DIT_ATTN_OK;
+}
+
 struct Fp8Layout {
   size_t q8, k8, v8t, sq, sk, sv, part, total;
   TailPlan plan;
@@ -280,6 +311,33 @@ int dit_attn_fwd_ws(const dit_attn_shape* shape, const void* q, const void* k, c
                                           static_cast<hipStream_t>(stream)),
                     "dit_attn_fwd_ws launch");
 }
+
+int dit_attn_fwd_noalloc(const dit_attn_shape* shape, const void* q, const void* k, const void* v, void* o,
+                         float* lse, void* stream) {
+  g_err[0] = '\0';
+  int rc = check_common(shape, q, k, v, o, lse);
+  if (rc) return rc;
+  const TailPlan t = tail_plan(shape, device_cus(), dit::kDenseRows, dit::kDenseTileKeys, true);
+  if (t.bytes > kNoallocScratchBytes)
+    return fail(DIT_ATTN_ERR_WORKSPACE,
+                "the tail split of this shape needs %zu bytes of scratch; the library's static scratch holds %zu",
+                t.bytes, kNoallocScratchBytes);
+  dit::AttnArgs a;
+  fill_common(shape, q, k, v, o, lse, a);
+  if (t.split > 1) {
+    void* ptr = nullptr;
+    if ((rc = scratch_device_ptr(&ptr))) return rc;
+    a.nfull = t.nfull;
+    a.ntail = t.ntail;
+    a.split = t.split;
+    a.part = static_cast<float*>(ptr);
+  }
+  return hip_status(dit::launch_attn_bf16(a, (shape->flags & DIT_ATTN_FLAG_OUT_F32) != 0, false,
+                                          static_cast<hipStream_t>(stream)),
+                    "dit_attn_fwd_noalloc launch");
+}
+
+size_t dit_attn_fwd_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
 
 size_t dit_attn_fwd_blocksparse_workspace_bytes(const dit_attn_shape* shape) {
   (void)shape;

@@ -27,7 +27,8 @@ def test_header_declares_the_expected_calls():
     for n in ("dit_attn_fwd", "dit_attn_fwd_ws", "dit_attn_fwd_workspace_bytes",
               "dit_attn_fwd_fp8", "dit_attn_fwd_fp8_workspace_bytes",
               "dit_attn_fp8_quantize", "dit_attn_fwd_blocksparse",
-              "dit_attn_fwd_blocksparse_workspace_bytes", "dit_attn_status_string",
+              "dit_attn_fwd_blocksparse_workspace_bytes", "dit_attn_fwd_noalloc",
+              "dit_attn_fwd_noalloc_scratch_bytes", "dit_attn_status_string",
               "dit_attn_last_error", "dit_attn_version"):
         assert n in names
 
@@ -186,6 +187,16 @@ def test_fp8_workspace_size_and_checks():
     g = lib.dit_attn_fp8_quantize
     s.head_dim = 128
     assert g(ctypes.byref(s), FAKE, FAKE, None, FAKE, need, None) == INVALID
+
+
+def test_noalloc_checks_arguments_before_any_device_call():
+    lib = dit.load()
+    assert lib.dit_attn_fwd_noalloc_scratch_bytes() == 64 << 20
+    bad = _shape()
+    bad.head_dim = 64
+    assert lib.dit_attn_fwd_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None, None) == UNSUPPORTED
+    assert lib.dit_attn_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
+    assert lib.dit_attn_fwd_noalloc(ctypes.byref(_shape()), FAKE, None, FAKE, FAKE, None, None) == INVALID
 
 
 def test_status_strings():
