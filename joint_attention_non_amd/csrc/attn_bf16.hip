@@ -30,7 +30,9 @@
 // rotating buffers.  Step t issues the QK^T MFMAs of tile t+1 and the PV
 // MFMAs of tile t as one stream with their LDS operands read ahead; the LDS
 // stores of tile t+2 and the global loads of tile t+3 ride on the PV MFMAs;
-// then one barrier, then the softmax of tile t+1.
+// then the softmax of tile t+1.  Waves 4-7 run half a step behind waves 0-3
+// (two barriers per step), so on each SIMD one wave's MFMA stream runs while
+// the other wave does its softmax.
 //
 // Tail split (dense, with a caller workspace): one 384-row work-group runs
 // per compute unit at a time, so the query blocks of a last, partial round
@@ -695,10 +697,11 @@ __device__ __forceinline__ float r_exp_block(const f32x4 (&sacc)[2][RRB], int rb
   for (int i = 0; i < 8; ++i) x[i] = fast_exp2(x[i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-  float ls0 = sum_bf16x2(pk[0], 0.f), ls1 = sum_bf16x2(pk[1], 0.f);
-  ls0 = sum_bf16x2(pk[2], ls0);
-  ls1 = sum_bf16x2(pk[3], ls1);
-  return ls0 + ls1;
+  // one accumulation chain: no zeroed accumulators to set up per pair
+  float ls = sum_bf16x2(pk[0], 0.f);
+  ls = sum_bf16x2(pk[1], ls);
+  ls = sum_bf16x2(pk[2], ls);
+  return sum_bf16x2(pk[3], ls);
 }
 
 __device__ __forceinline__ void r_mask(f32x4 (&sacc)[2][RRB], int key0, int N, int g) {
@@ -719,16 +722,31 @@ __device__ __forceinline__ void r_mask(f32x4 (&sacc)[2][RRB], int key0, int N, i
 // weights pass 2^64).
 __device__ __forceinline__ void r_softmax(f32x4 (&sacc)[2][RRB], RowState (&st)[RRB], f32x4 (&oacc)[8][RRB],
                                           uint32_t (&pk)[RRB][4], float c, bool first) {
+  // The three row blocks' weights are taken together (independent work for
+  // the vector ALU) and checked with one wave-wide test; only when some lane
+  // of some block passed the bound are the blocks revisited one by one.
+  float ls[RRB];
+  bool slow = first;
+  if (!first) {
+    bool ok = true;
 #pragma unroll
-  for (int rb = 0; rb < RRB; ++rb) {
-    float ls = 0.f;
-    if (!first) ls = r_exp_block(sacc, rb, st[rb].mc, c, pk[rb]);
-    if (first || __any(!(ls <= kCheck))) {
-      r_rescale(r_row_max(sacc, rb), st[rb], oacc, rb, c);
-      ls = r_exp_block(sacc, rb, st[rb].mc, c, pk[rb]);
+    for (int rb = 0; rb < RRB; ++rb) {
+      ls[rb] = r_exp_block(sacc, rb, st[rb].mc, c, pk[rb]);
+      ok = ok && (ls[rb] <= kCheck);
     }
-    st[rb].l += ls;
+    slow = __any(!ok);
   }
+  if (slow) {
+#pragma unroll
+    for (int rb = 0; rb < RRB; ++rb) {
+      if (first || __any(!(ls[rb] <= kCheck))) {
+        r_rescale(r_row_max(sacc, rb), st[rb], oacc, rb, c);
+        ls[rb] = r_exp_block(sacc, rb, st[rb].mc, c, pk[rb]);
+      }
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < RRB; ++rb) st[rb].l += ls[rb];
 }
 
 __device__ __forceinline__ void r_qk_tile(f32x4 (&sacc)[2][RRB], const __bf16* sK, const bf16x8 (&qf)[RRB][4],
@@ -840,6 +858,18 @@ __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
   r_softmax(sacc, st, oacc, pk, c, true);
 
   // ---- step t: QK^T of tile t+1 and PV of tile t, barrier, softmax of t+1 ----
+  // Ping-pong: waves 4-7 (one per SIMD) run half a step behind waves 0-3, so
+  // on every SIMD one wave's MFMA stream overlaps the other wave's softmax.
+  // Each step has two barriers: after the MFMA stream of waves 0-3 (and the
+  // softmax of waves 4-7), and after the softmax of waves 0-3 (and the MFMA
+  // stream of waves 4-7); waves 4-7 take one extra barrier before the loop
+  // and waves 0-3 one after it, so every wave passes the same number.  LDS
+  // buffer of tile t+2 = that of tile t-1, whose last readers (the PV MFMAs
+  // of step t-1 of both groups) are past the barrier that opens step t; tile
+  // t+2 is complete (both groups' halves stored) at the barrier that opens
+  // step t+1, before any QK^T of it.
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+  if (grp == 1) __syncthreads();
   int bc = 0;
   for (int t = t0; t + 1 < t1; ++t) {
     const int bn = (bc + 1 == RNB) ? 0 : bc + 1;
@@ -860,8 +890,10 @@ __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
     const int key1 = (t + 1) * RBN;
     if (key1 + RBN > N) r_mask(sacc, key1, N, g);
     r_softmax(sacc, st, oacc, pk, c, false);
+    __syncthreads();
     bc = bn;
   }
+  if (grp == 0) __syncthreads();
   // ---- drain: PV of the last tile ----
 #pragma unroll
   for (int db = 0; db < 8; ++db) {

@@ -13,7 +13,8 @@
 // Attention (work-group = 8 waves x 32 query rows, two waves per SIMD; key
 // tiles of 128 = one scale block, in three rotating LDS buffers; the QK^T
 // MFMAs of tile t+1 and the PV MFMAs of tile t form one stream with their
-// LDS operands read ahead, then one barrier, then the softmax of tile t+1),
+// LDS operands read ahead, then the softmax of tile t+1; waves 4-7 run half
+// a step behind waves 0-3, two barriers per step),
 // per tile with the 32x32x64 f8f6f4 MFMA:
 //   S^T = K8 Q8^T                    raw integer-grid dot products (fp32)
 //   t = S * (sQ sK scale log2 e)     logits in log2 units
@@ -384,8 +385,9 @@ __device__ __forceinline__ void softmax8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f
 // Work-group: NW waves x 32 query rows.  Step t issues the QK^T MFMAs of
 // tile t+1 and the PV MFMAs of tile t as one stream, their A operands read
 // from LDS kPre8 MFMAs ahead, with tile t+2 stored to LDS and tile t+3
-// loaded into registers beside the PV half; one barrier; then the softmax of
-// tile t+1.  Tiles rotate through NB8 LDS buffers.
+// loaded into registers beside the PV half; a barrier; then the softmax of
+// tile t+1 and a second barrier, with waves 4-7 half a step behind waves
+// 0-3.  Tiles rotate through NB8 LDS buffers.
 template <int NW, bool OUT_F32>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb) {
   constexpr int BM = NW * 32, NT = NW * 64;
@@ -457,6 +459,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
   qk8_tile(sacc, smK[0], qf, l32, h);
   softmax8(sacc, oacc, lacc, p8, m_run, unit, fq * skp[t0], svp[t0], a.p_off, t0 * BN8, N, h);
 
+  // Ping-pong, as in the bf16 dense kernel: waves 4-7 run half a step behind
+  // waves 0-3 (two barriers per step, one extra for each group outside the
+  // loop), so on every SIMD one wave's MFMAs overlap the other's softmax.
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+  if (grp == 1) __syncthreads();
   int bc = 0;   // LDS buffer of tile t; tile t+1 is in bc+1, tile t+2 goes to bc+2 (mod 3)
   for (int t = t0; t + 1 < t1; ++t) {
     const int bn = (bc + 1 == NB8) ? 0 : bc + 1;
@@ -476,8 +483,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
     step8_schedule<0>();
     __syncthreads();
     softmax8(sacc, oacc, lacc, p8, m_run, unit, fq * skp[t + 1], svp[t + 1], a.p_off, (t + 1) * BN8, N, h);
+    __syncthreads();
     bc = bn;
   }
+  if (grp == 0) __syncthreads();
   pv8_tile(oacc, lacc, p8, smV[bc], l32, h);
 
   // ---- epilogue: O = A * sV_last / l ----
