@@ -5,11 +5,13 @@
 //                    whole kernel.
 //   online softmax   P = 2^(S c - m c) with c = scale * log2(e) and m a
 //                    running reference: the row max of the first tile.  Later
-//                    tiles take their exponentials against it directly; only
-//                    when a lane's weights would pass 2^64 (a row max that
-//                    grew by more than 64 bits) is m moved to the new max,
-//                    O and l rescaled and the tile redone.  The factor
-//                    cancels in O / l, so the result is unchanged.
+//                    tiles take their exponentials against it directly: P
+//                    far above 1 is harmless in fp32 (l and O keep their
+//                    relative precision), and the reference is moved to a
+//                    new max (O and l rescaled, the work redone) only when
+//                    the weights grow past a bound -- per tile (2^64, the
+//                    block-sparse kernel) or per row at the end (2^80, the
+//                    dense kernel).  The factor cancels in O / l.
 //   O^T += V^T P^T   A = V^T, read from the row-major V tile with the gfx950
 //                    transposing LDS read (ds_read_b64_tr_b16: 16 lanes
 //                    fetch a 4-key x 16-d block and each lane receives one d
@@ -18,7 +20,10 @@
 //                    permuted instead, by choosing which 4 keys each
 //                    transposing read fetches to match the order in which
 //                    the accumulator hands P out.  l accumulates the same
-//                    rounded P (v_dot2 with (1, 1)).
+//                    rounded P: v_dot2 with (1, 1) in the block-sparse
+//                    kernel, one extra MFMA per 32-key tile and row block
+//                    with an all-ones A operand in the dense kernel (every
+//                    row of its result is the column sum of P^T).
 // Epilogue: O = O^T / l, stored bf16 (round to nearest even) or fp32, and
 // optionally lse = ln2 * (m c + log2 l).
 //
@@ -50,6 +55,8 @@
 
 #include "device_common.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace dit {
 namespace {
@@ -243,6 +250,8 @@ __device__ __forceinline__ float exp_tile_sum(const f32x16 (&sacc)[2], float mc,
 // per-tile row max out of the common path.
 // `first` (wave-uniform) forces the max pass, for the first tile of a row.
 constexpr float kCheck = 0x1p64f;   // 2^64
+// The dense kernel checks each row's whole weight sum once, at the end.
+constexpr float kEndCheck = 0x1p80f;
 __device__ __forceinline__ void softmax_next(const f32x16 (&sacc)[2], RowState& st, f32x16 (&oacc)[4],
                                              uint32_t (&pk)[2][8], float c, bool first = false) {
   float ls = exp_tile_sum(sacc, st.mc, pk, c);
@@ -615,7 +624,8 @@ constexpr int kRPre = 3;   // operand pairs read this many steps ahead (2-4 meas
 // staging, the K and V chunks of the staged tile are stored at I = 8 and 12
 // and the registers refilled with the tile after it.
 template <int I>
-__device__ __forceinline__ void r_step(f32x4 (&sacc)[2][RRB], f32x4 (&oacc)[8][RRB], const bf16x8 (&qf)[RRB][4],
+__device__ __forceinline__ void r_step(f32x4 (&sacc)[2][RRB], f32x4 (&oacc)[8][RRB], f32x4 (&lacc)[RRB],
+                                       const bf16x8& ones, const bf16x8 (&qf)[RRB][4],
                                        const uint32_t (&pk)[RRB][4], const __bf16* sK, const __bf16* sV, int l16,
                                        int g, int s, bf16x8 (&fr)[kRPre + 1], RLoader& ld, __bf16* sks, __bf16* svs,
                                        __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t krow,
@@ -632,6 +642,8 @@ __device__ __forceinline__ void r_step(f32x4 (&sacc)[2][RRB], f32x4 (&oacc)[8][R
 #pragma unroll
       for (int rb = 0; rb < RRB; ++rb) oacc[db][rb] = mfma16(a, r_p_operand(pk[rb]), oacc[db][rb]);
       if constexpr (I == 8) {
+#pragma unroll
+        for (int rb = 0; rb < RRB; ++rb) lacc[rb] = mfma16(ones, r_p_operand(pk[rb]), lacc[rb]);
         ld.template store_one<0>(sks, svs, tid);
         ld.template load_one<0>(rk, rv, krow, vrow, kload, N, tid);
       }
@@ -640,7 +652,8 @@ __device__ __forceinline__ void r_step(f32x4 (&sacc)[2][RRB], f32x4 (&oacc)[8][R
         ld.template load_one<1>(rk, rv, krow, vrow, kload, N, tid);
       }
     }
-    r_step<I + 1>(sacc, oacc, qf, pk, sK, sV, l16, g, s, fr, ld, sks, svs, rk, rv, krow, vrow, kload, N, tid);
+    r_step<I + 1>(sacc, oacc, lacc, ones, qf, pk, sK, sV, l16, g, s, fr, ld, sks, svs, rk, rv, krow, vrow, kload, N,
+                  tid);
   }
 }
 
@@ -648,7 +661,7 @@ template <int I>
 __device__ __forceinline__ void r_step_schedule() {
   if constexpr (I < 16) {
     if constexpr (I + kRPre < 16) __builtin_amdgcn_sched_group_barrier(0x100, I + kRPre < 8 ? 1 : 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, RRB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, I == 8 ? 2 * RRB : RRB, 0);
     if constexpr (I == 8 || I == 12) {
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -670,12 +683,14 @@ __device__ __forceinline__ float r_row_sum(float x) {
   return x + swap_halves(x);
 }
 
-__device__ __forceinline__ void r_rescale(float t, RowState& st, f32x4 (&oacc)[8][RRB], int rb, float c) {
+__device__ __forceinline__ void r_rescale(float t, RowState& st, f32x4 (&oacc)[8][RRB], f32x4 (&lacc)[RRB], int rb,
+                                          float c) {
   const bool grow = (t - st.m) * c > kLazy;
   if (__any(grow)) {
     const float mnew = fmaxf(st.m, t);
     const float alpha = fast_exp2((st.m - mnew) * c);
-    st.l *= alpha;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lacc[rb][r] *= alpha;
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
@@ -688,8 +703,8 @@ __device__ __forceinline__ void r_rescale(float t, RowState& st, f32x4 (&oacc)[8
 // P for row block rb: 2^(S c - mc) rounded to bf16 pairs in the B-operand
 // order (keys 4g..4g+3, then 16+4g..16+4g+3); returns the lane's sum of the
 // rounded P.
-__device__ __forceinline__ float r_exp_block(const f32x4 (&sacc)[2][RRB], int rb, float mc, float c,
-                                             uint32_t (&pk)[4]) {
+__device__ __forceinline__ void r_exp_block(const f32x4 (&sacc)[2][RRB], int rb, float mc, float c,
+                                            uint32_t (&pk)[4]) {
   float x[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(sacc[i >> 2][rb][i & 3], c, -mc);
@@ -697,11 +712,6 @@ __device__ __forceinline__ float r_exp_block(const f32x4 (&sacc)[2][RRB], int rb
   for (int i = 0; i < 8; ++i) x[i] = fast_exp2(x[i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-  // one accumulation chain: no zeroed accumulators to set up per pair
-  float ls = sum_bf16x2(pk[0], 0.f);
-  ls = sum_bf16x2(pk[1], ls);
-  ls = sum_bf16x2(pk[2], ls);
-  return sum_bf16x2(pk[3], ls);
 }
 
 __device__ __forceinline__ void r_mask(f32x4 (&sacc)[2][RRB], int key0, int N, int g) {
@@ -721,32 +731,13 @@ __device__ __forceinline__ void r_mask(f32x4 (&sacc)[2][RRB], int key0, int N, i
 // the reference first; later tiles keep the reference unless a lane's
 // weights pass 2^64).
 __device__ __forceinline__ void r_softmax(f32x4 (&sacc)[2][RRB], RowState (&st)[RRB], f32x4 (&oacc)[8][RRB],
-                                          uint32_t (&pk)[RRB][4], float c, bool first) {
-  // The three row blocks' weights are taken together (independent work for
-  // the vector ALU) and checked with one wave-wide test; only when some lane
-  // of some block passed the bound are the blocks revisited one by one.
-  float ls[RRB];
-  bool slow = first;
-  if (!first) {
-    bool ok = true;
+                                          f32x4 (&lacc)[RRB], uint32_t (&pk)[RRB][4], float c, bool exact) {
+  if (exact) {
 #pragma unroll
-    for (int rb = 0; rb < RRB; ++rb) {
-      ls[rb] = r_exp_block(sacc, rb, st[rb].mc, c, pk[rb]);
-      ok = ok && (ls[rb] <= kCheck);
-    }
-    slow = __any(!ok);
-  }
-  if (slow) {
-#pragma unroll
-    for (int rb = 0; rb < RRB; ++rb) {
-      if (first || __any(!(ls[rb] <= kCheck))) {
-        r_rescale(r_row_max(sacc, rb), st[rb], oacc, rb, c);
-        ls[rb] = r_exp_block(sacc, rb, st[rb].mc, c, pk[rb]);
-      }
-    }
+    for (int rb = 0; rb < RRB; ++rb) r_rescale(r_row_max(sacc, rb), st[rb], oacc, lacc, rb, c);
   }
 #pragma unroll
-  for (int rb = 0; rb < RRB; ++rb) st[rb].l += ls[rb];
+  for (int rb = 0; rb < RRB; ++rb) r_exp_block(sacc, rb, st[rb].mc, c, pk[rb]);
 }
 
 __device__ __forceinline__ void r_qk_tile(f32x4 (&sacc)[2][RRB], const __bf16* sK, const bf16x8 (&qf)[RRB][4],
@@ -821,17 +812,6 @@ __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
       qf[rb][ds] = __builtin_bit_cast(bf16x8, buf_load_b128(rq, (uint32_t)row * qrow + (32 * ds + 8 * g) * 2));
     }
 
-  f32x4 oacc[8][RRB];
-#pragma unroll
-  for (int db = 0; db < 8; ++db)
-#pragma unroll
-    for (int rb = 0; rb < RRB; ++rb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[db][rb][r] = 0.f;
-  RowState st[RRB];
-#pragma unroll
-  for (int rb = 0; rb < RRB; ++rb) st[rb] = {-INFINITY, 0.f, 0.f};
-
   // Key tiles [t0, t1) of T; part p of `split` takes t = p T / split ..
   // (p + 1) T / split (never empty: split <= T).
   const int T = (N + RBN - 1) / RBN;
@@ -840,73 +820,100 @@ __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
     t0 = part * T / a.split;
     t1 = (part + 1) * T / a.split;
   }
-
-  // ---- prologue: tiles t0 and t0+1 into LDS, t0+2 into registers (loads
-  // past N read as zero; tiles past t1 are never used) ----
-  RLoader ld;
-  ld.load(rk, rv, krow, vrow, t0 * RBN, N, tid);
-  ld.store(smK[0], smV[0], tid);
-  ld.load(rk, rv, krow, vrow, (t0 + 1) * RBN, N, tid);
-  ld.store(smK[1], smV[1], tid);
-  ld.load(rk, rv, krow, vrow, (t0 + 2) * RBN, N, tid);
-  __syncthreads();
-
-  f32x4 sacc[2][RRB];
-  uint32_t pk[RRB][4];
-  r_qk_tile(sacc, smK[0], qf, l16, g);
-  if ((t0 + 1) * RBN > N) r_mask(sacc, t0 * RBN, N, g);
-  r_softmax(sacc, st, oacc, pk, c, true);
-
-  // ---- step t: QK^T of tile t+1 and PV of tile t, barrier, softmax of t+1 ----
-  // Ping-pong: waves 4-7 (one per SIMD) run half a step behind waves 0-3, so
-  // on every SIMD one wave's MFMA stream overlaps the other wave's softmax.
-  // Each step has two barriers: after the MFMA stream of waves 0-3 (and the
-  // softmax of waves 4-7), and after the softmax of waves 0-3 (and the MFMA
-  // stream of waves 4-7); waves 4-7 take one extra barrier before the loop
-  // and waves 0-3 one after it, so every wave passes the same number.  LDS
-  // buffer of tile t+2 = that of tile t-1, whose last readers (the PV MFMAs
-  // of step t-1 of both groups) are past the barrier that opens step t; tile
-  // t+2 is complete (both groups' halves stored) at the barrier that opens
-  // step t+1, before any QK^T of it.
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
-  if (grp == 1) __syncthreads();
+  const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                       (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+
+  f32x4 oacc[8][RRB];
+  f32x4 lacc[RRB];   // row sums of the rounded P (every element of a row block's C holds its row's sum)
+  RowState st[RRB];
   int bc = 0;
-  for (int t = t0; t + 1 < t1; ++t) {
-    const int bn = (bc + 1 == RNB) ? 0 : bc + 1;
-    const int bn2 = (bn + 1 == RNB) ? 0 : bn + 1;
+  // Pass 0 takes every tile after the first against the first tile's row max
+  // (no per-tile max, no per-tile check).  Weights far above 1 are harmless
+  // in fp32 as long as nothing overflows: if some row's weight sum ends at
+  // most 2^80, every weight was at most 2^80 and the row's unnormalised O is
+  // at most 2^80 max|V| (finite for |V| below 2.8e14), and the result is
+  // kept.  Otherwise (the reference lagged the row max by more than about
+  // 80 bits somewhere, or a weight overflowed) the work-group runs its key
+  // range again (EXACT pass) with the row max taken on every tile, so that
+  // no weight exceeds 2^8.  Two copies of the loop, so that the common one
+  // carries no per-tile max code.
+  auto run_pass = [&](auto exact_tag) {
+    constexpr bool EXACT = decltype(exact_tag)::value;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int rb = 0; rb < RRB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sacc[kb][rb][r] = 0.f;
-    bf16x8 fr[kRPre + 1];
-    r_prefetch<0, kRPre>(fr, smK[bn], smV[bc], l16, g, s);
-    r_step<0>(sacc, oacc, qf, pk, smK[bn], smV[bc], l16, g, s, fr, ld, smK[bn2], smV[bn2], rk, rv, krow, vrow,
-              (t + 3) * RBN, N, tid);
-    __builtin_amdgcn_sched_group_barrier(0x100, kRPre, 0);
-    r_step_schedule<0>();
-    __syncthreads();
-    const int key1 = (t + 1) * RBN;
-    if (key1 + RBN > N) r_mask(sacc, key1, N, g);
-    r_softmax(sacc, st, oacc, pk, c, false);
-    __syncthreads();
-    bc = bn;
-  }
-  if (grp == 0) __syncthreads();
-  // ---- drain: PV of the last tile ----
+        for (int r = 0; r < 4; ++r) oacc[db][rb][r] = 0.f;
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    const bf16x8 vf = r_v_operand(smV[bc], db, g, s);
+    for (int rb = 0; rb < RRB; ++rb) {
+      st[rb] = {-INFINITY, 0.f, 0.f};
 #pragma unroll
-    for (int rb = 0; rb < RRB; ++rb) oacc[db][rb] = mfma16(vf, r_p_operand(pk[rb]), oacc[db][rb]);
-  }
+      for (int r = 0; r < 4; ++r) lacc[rb][r] = 0.f;
+    }
+
+    // ---- prologue: tiles t0 and t0+1 into LDS, t0+2 into registers ----
+    RLoader ld;
+    ld.load(rk, rv, krow, vrow, t0 * RBN, N, tid);
+    ld.store(smK[0], smV[0], tid);
+    ld.load(rk, rv, krow, vrow, (t0 + 1) * RBN, N, tid);
+    ld.store(smK[1], smV[1], tid);
+    ld.load(rk, rv, krow, vrow, (t0 + 2) * RBN, N, tid);
+    __syncthreads();
+
+    f32x4 sacc[2][RRB];
+    uint32_t pk[RRB][4];
+    r_qk_tile(sacc, smK[0], qf, l16, g);
+    if ((t0 + 1) * RBN > N) r_mask(sacc, t0 * RBN, N, g);
+    r_softmax(sacc, st, oacc, lacc, pk, c, true);
+
+    if (grp == 1) __syncthreads();
+    bc = 0;
+    for (int t = t0; t + 1 < t1; ++t) {
+      const int bn = (bc + 1 == RNB) ? 0 : bc + 1;
+      const int bn2 = (bn + 1 == RNB) ? 0 : bn + 1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RRB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[kb][rb][r] = 0.f;
+      bf16x8 fr[kRPre + 1];
+      r_prefetch<0, kRPre>(fr, smK[bn], smV[bc], l16, g, s);
+      r_step<0>(sacc, oacc, lacc, ones, qf, pk, smK[bn], smV[bc], l16, g, s, fr, ld, smK[bn2], smV[bn2], rk, rv,
+                krow, vrow, (t + 3) * RBN, N, tid);
+      __builtin_amdgcn_sched_group_barrier(0x100, kRPre, 0);
+      r_step_schedule<0>();
+      __syncthreads();
+      const int key1 = (t + 1) * RBN;
+      if (key1 + RBN > N) r_mask(sacc, key1, N, g);
+      r_softmax(sacc, st, oacc, lacc, pk, c, EXACT);
+      __syncthreads();
+      bc = bn;
+    }
+    if (grp == 0) __syncthreads();
+    // ---- drain: PV of the last tile ----
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 vf = r_v_operand(smV[bc], db, g, s);
+#pragma unroll
+      for (int rb = 0; rb < RRB; ++rb) oacc[db][rb] = mfma16(vf, r_p_operand(pk[rb]), oacc[db][rb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RRB; ++rb) lacc[rb] = mfma16(ones, r_p_operand(pk[rb]), lacc[rb]);
+  };
+  run_pass(std::false_type{});
+  bool ok = true;
+#pragma unroll
+  for (int rb = 0; rb < RRB; ++rb) ok = ok && (lacc[rb][0] <= kEndCheck);
+  if (__syncthreads_or(!ok)) run_pass(std::true_type{});
 
   // ---- epilogue: lane (g, l16) holds d = 16 db + 4 g + r of row q0 + 16 rb + l16 ----
   const int64_t ob = b * a.os[0] + hd * a.os[1];
 #pragma unroll
   for (int rb = 0; rb < RRB; ++rb) {
-    const float lt = r_row_sum(st[rb].l);
+    const float lt = lacc[rb][0];
     const int row = q0 + 16 * rb + l16;
     if (row >= N) continue;
     if (part >= 0) {
