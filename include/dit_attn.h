@@ -159,8 +159,12 @@ size_t dit_attn_fwd_fp8_workspace_bytes(const dit_attn_shape* shape);
  * probabilities w in [0, 1] are quantised as e4m3(448 w) for the fp8 PV
  * product, and the row sum is taken over the same quantised weights (so the
  * normalised weights sum to one); output is bf16 (or fp32).
- * The quantisation pass writes the workspace (layout above), then the
- * attention pass reads it, both on `stream`.  As in dit_attn_fwd_ws, the
+ * The quantisation pass writes the K and V regions of the workspace (layout
+ * above), then the attention pass reads them, both on `stream`; Q is
+ * quantised inside the attention kernel (each of its 256-row work-groups
+ * owns two whole 128-token scale blocks), with the same arithmetic and
+ * codes, so the Q8 and sQ regions are left untouched (dit_attn_fp8_quantize
+ * fills them).  As in dit_attn_fwd_ws, the
  * 256-row query blocks of a last partial round are split over key ranges,
  * each with its own running max, and merged with exact rescaling; their P
  * is therefore rounded against a different running max than in one pass. */
@@ -169,8 +173,9 @@ int dit_attn_fwd_fp8(const dit_attn_shape* shape,
                      void* o, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Only the quantisation pass of dit_attn_fwd_fp8: fills the workspace (same
- * layout) so a caller can inspect or reuse the e4m3 codes and scales. */
+/* The quantisation of dit_attn_fwd_fp8 alone, for Q, K and V: fills every
+ * region of the workspace but the tail-split scratch (same layout) so a
+ * caller can inspect or reuse the e4m3 codes and scales. */
 int dit_attn_fp8_quantize(const dit_attn_shape* shape,
                           const void* q, const void* k, const void* v,
                           void* workspace, size_t workspace_bytes, void* stream);

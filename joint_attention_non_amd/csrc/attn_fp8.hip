@@ -1,5 +1,7 @@
 // attn_fp8.hip -- fp8 (OCP e4m3) joint attention for gfx950: a quantisation
-// pass over Q, K, V and a flash-style attention kernel on the fp8 MFMA.
+// pass over K and V (and Q, for the quantise-only entry point) and a
+// flash-style attention kernel on the fp8 MFMA that quantises its own Q
+// rows in its prologue.
 //
 // Quantisation (one work-group per tensor x (b, h) x 128-token block):
 //   absmax over the block (fp32), inv = 448 / absmax, s = absmax / 448,
@@ -40,6 +42,12 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, 64));
+  return x;
+}
+
 // Position group (4 keys) inside a 64-key group of V8t for key group kg.
 __device__ __forceinline__ int v8_pos_group(int kg) {
   return 8 * (kg & 1) + 4 * (kg >> 3) + ((kg >> 1) & 3);
@@ -64,7 +72,7 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(Fp8Args a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int BH = a.B * a.H;
   const int id = blockIdx.x;
-  const int tensor = id / (BH * a.nb);
+  const int tensor = a.first_tensor + id / (BH * a.nb);
   const int rem = id % (BH * a.nb);
   const int bh = rem / a.nb, kb = rem % a.nb;
   const int b = bh / a.H, hd = bh % a.H;
@@ -393,6 +401,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
   constexpr int BM = NW * 32, NT = NW * 64;
   __shared__ __attribute__((aligned(16))) uint8_t smK[NB8][BN8 * RS8];
   __shared__ __attribute__((aligned(16))) uint8_t smV[NB8][D * RS8];
+  __shared__ uint32_t qmax_lds[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -412,27 +421,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
   const int t0 = part < 0 ? 0 : part * nb / a.split;
   const int t1 = part < 0 ? nb : (part + 1) * nb / a.split;
 
-  const uint8_t* q8 = a.q8 + (int64_t)bh * np * D;
   const uint8_t* k8 = a.k8 + (int64_t)bh * np * D;
   const uint8_t* v8 = a.v8t + (int64_t)bh * D * np;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q8, (uint32_t)(np * D));
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k8, (uint32_t)(np * D));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v8, (uint32_t)(np * D));
-
-  const int q0 = qblk * BM + wave * 32;
-  const float sqw = (q0 < np) ? a.sq[(int64_t)bh * nb + q0 / kBlock] : 1.f;
-  const float fq = sqw * a.c;
   const float* skp = a.sk + (int64_t)bh * nb;
   const float* svp = a.sv + (int64_t)bh * nb;
 
-  // Q8 as the B operand: lane (l32, h) holds row q0 + l32, d = 64 s + 32 h .. +31.
-  i32x8 qf[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const uint32_t off = (uint32_t)(q0 + l32) * D + 64 * s + 32 * h;
-    const u32x4 lo = buf_load_b128(rq, off), hi = buf_load_b128(rq, off + 16);
-    qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  }
+  // Q is quantised here, in the prologue, rather than by the quantisation
+  // pass: the work-group's 256 rows are exactly two 128-token scale blocks
+  // (waves 0-3 and 4-7), so each block's absmax is a reduction inside the
+  // work-group.  Same arithmetic as the pass, hence the same codes and
+  // scale.  Lane (l32, h) loads row q0 + l32, d = 64 s + 32 h .. +31 (bf16;
+  // rows >= N read as zero and leave the absmax alone), which is exactly
+  // the part of Q8 it needs as the B operand.
+  const int q0 = qblk * BM + wave * 32;
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.qs[0] + hd * a.qs[1];
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qp, a.q_bytes);
+  const uint32_t qoff = (uint32_t)min(q0 + l32, N) * (uint32_t)(a.qs[2] * 2);
 
   f32x16 oacc[4];
   f32x16 lacc;   // row sums of the quantised weights (448 units), element 0 used
@@ -448,11 +454,55 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
   // ---- prologue: tiles t0 and t0+1 into LDS, t0+2 into registers ----
   Loader8<NT> ld;
   ld.load(rk, rv, t0, np, tid);
+  u32x4 qx[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) qx[s][c4] = buf_load_b128(rq, qoff + (64 * s + 32 * h + 8 * c4) * 2);
   ld.store(smK[0], smV[0], tid);
   ld.load(rk, rv, min(t0 + 1, t1 - 1), np, tid);
+  uint32_t qabs = 0;   // max of |x| over this lane's elements, as bf16 bits (ordered like the values)
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t m = qx[s][c4][w] & 0x7fff7fffu;
+        qabs = max(qabs, max(m & 0xffffu, m >> 16));
+      }
+  qabs = wave_max_u32(qabs);
+  if (lane == 0) qmax_lds[wave] = qabs;
   ld.store(smK[1], smV[1], tid);
   ld.load(rk, rv, min(t0 + 2, t1 - 1), np, tid);
   __syncthreads();
+
+  // The Q scale block of this wave: absmax over its four waves, then the
+  // quantisation pass's rule (448 / absmax in fp32, codes e4m3(clamp(x *
+  // inv)), a block whose 448 / absmax is not finite stored as zero codes
+  // with scale 1).
+  const int w0 = wave & 4;
+  const uint32_t qbits = max(max(qmax_lds[w0], qmax_lds[w0 + 1]), max(qmax_lds[w0 + 2], qmax_lds[w0 + 3]));
+  const float qamax = __builtin_bit_cast(float, qbits << 16);
+  const float qinv = 448.0f / qamax;
+  const bool qzero = !(qinv <= 3.40282347e38f);
+  const float fq = (qzero ? 1.0f : qamax / 448.0f) * a.c;
+  i32x8 qf[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t w = qx[s][c4][2 * hf + e];
+          y[2 * e] = fminf(fmaxf(bf16_lo(w) * qinv, -448.f), 448.f);
+          y[2 * e + 1] = fminf(fmaxf(bf16_hi(w) * qinv, -448.f), 448.f);
+        }
+        qf[s][2 * c4 + hf] = qzero ? 0 : (int)cvt4_e4m3(y[0], y[1], y[2], y[3]);
+      }
 
   f32x16 sacc[4];
   uint32_t p8[2][8];
@@ -540,7 +590,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
 }  // namespace
 
 hipError_t launch_fp8_quantize(const Fp8Args& a, hipStream_t s) {
-  const int64_t nwg = 3LL * a.B * a.H * a.nb;
+  const int64_t nwg = (3LL - a.first_tensor) * a.B * a.H * a.nb;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
   return launch_kernel(fp8_quantize_kernel, dim3((unsigned)nwg), dim3(256), s, a);
 }

@@ -392,6 +392,7 @@ int dit_attn_fwd_fp8(const dit_attn_shape* shape, const void* q, const void* k, 
   int rc = prepare_fp8(shape, q, k, v, o, lse, workspace, workspace_bytes, true, f);
   if (rc) return rc;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  f.first_tensor = 1;   // the attention kernel quantises Q in its prologue
   rc = hip_status(dit::launch_fp8_quantize(f, s), "fp8 quantise launch");
   if (rc) return rc;
   return hip_status(dit::launch_attn_fp8(f, (shape->flags & DIT_ATTN_FLAG_OUT_F32) != 0, s), "fp8 attention launch");

@@ -58,6 +58,7 @@ struct Fp8Args {
   float* sv;
   float c;              // softmax_scale * log2(e)
   float p_off;          // just below log2(448): w * 448 = exp2(x + p_off) <= 448
+  int first_tensor;     // quantisation pass: 0 = Q, K and V; 1 = K and V (the attention quantises Q itself)
   // Tail split of the attention grid, as for AttnArgs (split == 1: none).
   int nfull, ntail, split;
   float* part;          // [ntail * split][bm rows][kPartRow] fp32
