@@ -200,9 +200,10 @@ size_t dit_attn_fwd_blocksparse_workspace_bytes(const dit_attn_shape* shape);
  * least dit_attn_fwd_blocksparse_workspace_bytes(shape) bytes, 256-byte
  * aligned (NULL when that is 0); ERR_WORKSPACE otherwise.
  * The per-tile arithmetic is that of dit_attn_fwd (fp32 scores, P rounded
- * to bf16, row sums over the rounded P) in 64-key tiles on 128-row blocks,
- * so an all-ones mask reproduces dit_attn_fwd within the same tolerance, not
- * bit for bit. */
+ * to bf16, row sums over the rounded P, 32-key tiles) on 128-row blocks, so
+ * an all-ones mask reproduces dit_attn_fwd within the same tolerance, not
+ * bit for bit (the first-tile reference differs: the two kernels group rows
+ * differently). */
 int dit_attn_fwd_blocksparse(const dit_attn_shape* shape,
                              const void* q, const void* k, const void* v,
                              void* o, float* lse,
