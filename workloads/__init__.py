@@ -21,8 +21,9 @@ The token order is text first, then image latents: joint attention in the
 FLUX-family DiT concatenates the separately embedded text, target-image and
 optional reference-image streams and runs one attention over all of them
 (bpdata.com "FLUX 3 Image Klein optimalizálása", section "Modellezés és
-pipeline jellemzők").  Seed 0 throughout, as the pages' benchmarks use a fixed
-seed 0 (same page, same section).
+pipeline jellemzők").  Seed 0 throughout: that section states that the
+benchmarks were run with seed 0, and the page's run example passes --seed 0
+(section "Telepítési és futtatási példák").
 
 Random-number recipe (stated once, used by tests, smoke and the benchmark):
 
