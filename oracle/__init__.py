@@ -22,8 +22,14 @@ Functions and what pins them (tests/test_oracle.py):
   e4m3 step, zero block) and against torch's float8 cast.
 * ``attn_fp8_recipe``   -- the fp8 attention recipe; with P quantisation off it
   must equal ``attn`` on the dequantised inputs, with it on a one-hot key must
-  return the dequantised value row exactly, and its error against ``attn`` on
-  the unquantised inputs must sit in the band the e4m3 step implies.
+  return the dequantised value row exactly, its running max across key blocks
+  must match a restatement with torch's e4m3 cast (and differ from the
+  final-max variant), and its error against ``attn`` on the unquantised inputs
+  must sit in the band the e4m3 step implies.
+* ``select_blocks``     -- the block-mask selection rule; pinned against
+  torch's block pooling and scipy's softmax, the softmax's shift invariance,
+  key-block permutation, identical key blocks (every share exactly 1/nb),
+  tau = 0, and a planted dominant block.
 """
 from __future__ import annotations
 
@@ -68,6 +74,9 @@ def _load():
         lib.oracle_attn_fp8_recipe.argtypes = [i64, i64, i64, i64, u8p, u8p, u8p, fp, fp, fp,
                                                ctypes.c_double, ctypes.c_int, dp, i64, dp, dp]
         lib.oracle_attn_fp8_recipe.restype = ctypes.c_int
+        lib.oracle_select_blocks.argtypes = [i64, i64, i64, i64, dp, dp, ctypes.c_double,
+                                             ctypes.c_double, i64, u8p, dp]
+        lib.oracle_select_blocks.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -194,3 +203,18 @@ def attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale: float, quantize_p: bool = Tru
     if rows is None:
         return o.reshape(B, H, N, D), lse.reshape(B, H, N)
     return o, lse
+
+
+def select_blocks(q, k, scale: float, tau: float, text_tokens: int, block: int = 128):
+    """Sol-Attention-style block selection (see attn_oracle.c): returns
+    (mask uint8 [B, H, nb, nb], share float64 [B, H, nb, nb])."""
+    qd, kd = _as_f64(q), _as_f64(k)
+    if qd.ndim != 4 or kd.shape != qd.shape:
+        raise ValueError("q, k must be [B, H, N, D] of one shape")
+    B, H, N, D = qd.shape
+    nb = (N + block - 1) // block
+    mask = np.empty((B, H, nb, nb), dtype=np.uint8)
+    share = np.empty((B, H, nb, nb), dtype=np.float64)
+    _load().oracle_select_blocks(B * H, N, D, block, _ptr(qd), _ptr(kd), float(scale), float(tau),
+                                 int(text_tokens), _ptr(mask), _ptr(share))
+    return mask, share

@@ -299,6 +299,68 @@ int oracle_attn_fp8_recipe(int64_t BH, int64_t N, int64_t D, int64_t block,
     return bad ? -1 : 0;
 }
 
+/* Block-mask selection in the manner of Sol-Attention (block-sparse attention
+ * whose sparsity a parameter tau controls: bpdata.com page, section
+ * "Részletes optimalizációs lépések és hatásuk"; the rule itself is a reading,
+ * stated here in full because the pages do not give one).  For one (b, h):
+ *
+ *   qm_i = mean of q over the valid tokens of query block i   (fp64)
+ *   km_j = mean of k over the valid tokens of key block j
+ *   s_ij = scale * <qm_i, km_j>
+ *   p_ij = exp(s_ij - max_j s_ij) / sum_j exp(s_ij - max_j s_ij)
+ *   keep_ij = p_ij >= tau / nb   or   i == j   or   i < tb   or   j < tb
+ *
+ * with nb = ceil(N / block) and tb = ceil(text_tokens / block): a key block
+ * is kept when its estimated share of the row's attention is at least tau
+ * times the uniform share; the diagonal and the text blocks' rows and
+ * columns are always kept.  q, k: [BH][N][D] doubles.  mask: uint8
+ * [BH][nb][nb]; share (nullable): [BH][nb][nb] doubles, the p_ij. */
+void oracle_select_blocks(int64_t BH, int64_t N, int64_t D, int64_t block,
+                          const double* q, const double* k, double scale, double tau,
+                          int64_t text_tokens, uint8_t* mask, double* share)
+{
+    const int64_t nb = (N + block - 1) / block, tb = (text_tokens + block - 1) / block;
+#pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        double* qm = (double*)calloc((size_t)(nb * D), sizeof(double));
+        double* km = (double*)calloc((size_t)(nb * D), sizeof(double));
+        double* s = (double*)malloc(sizeof(double) * (size_t)nb);
+        if (!qm || !km || !s) { free(qm); free(km); free(s); continue; }
+        for (int64_t b = 0; b < nb; ++b) {
+            const int64_t j0 = b * block, j1 = (j0 + block < N) ? j0 + block : N;
+            for (int64_t j = j0; j < j1; ++j)
+                for (int64_t d = 0; d < D; ++d) {
+                    qm[b * D + d] += q[(bh * N + j) * D + d];
+                    km[b * D + d] += k[(bh * N + j) * D + d];
+                }
+            for (int64_t d = 0; d < D; ++d) {
+                qm[b * D + d] /= (double)(j1 - j0);
+                km[b * D + d] /= (double)(j1 - j0);
+            }
+        }
+        for (int64_t i = 0; i < nb; ++i) {
+            double m = -INFINITY;
+            for (int64_t j = 0; j < nb; ++j) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d) dot += qm[i * D + d] * km[j * D + d];
+                s[j] = scale * dot;
+                if (s[j] > m) m = s[j];
+            }
+            double z = 0.0;
+            for (int64_t j = 0; j < nb; ++j) z += exp(s[j] - m);
+            for (int64_t j = 0; j < nb; ++j) {
+                const double p = exp(s[j] - m) / z;
+                const int forced = (i == j) || (i < tb) || (j < tb);
+                mask[(bh * nb + i) * nb + j] = (uint8_t)((p >= tau / (double)nb) || forced);
+                if (share) share[(bh * nb + i) * nb + j] = p;
+            }
+        }
+        free(qm);
+        free(km);
+        free(s);
+    }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -473,3 +473,97 @@ def test_fp8_quantize_tiny_block_is_a_zero_block():
     assert np.isfinite(np.float32(448.0) / amax1)
     assert scales[0, 1, 0] == amax1 / np.float32(448.0)
     assert np.max(np.abs(oracle.e4m3_decode_array(codes[0, 1, :128]))) == 448.0
+
+
+# ----------------------------------------------------------------------------
+# block-mask selection (tau rule)
+# ----------------------------------------------------------------------------
+
+def _library_select(q, k, scale, tau, text_tokens, block=128):
+    """The rule from library steps: block means by torch's avg_pool1d (the
+    ragged last block through its own call), scipy's softmax, the threshold
+    and the forced blocks."""
+    B, H, N, D = q.shape
+    nb = (N + block - 1) // block
+
+    def pool(x):
+        x = x.to(torch.float64).reshape(B * H, N, D).transpose(1, 2)      # [BH, D, N]
+        full = (N // block) * block
+        parts = []
+        if full:
+            parts.append(F.avg_pool1d(x[:, :, :full], block))
+        if N > full:
+            parts.append(F.avg_pool1d(x[:, :, full:], N - full))
+        return torch.cat(parts, dim=2).transpose(1, 2).numpy()           # [BH, nb, D]
+
+    qm, km = pool(q), pool(k)
+    s = scale * np.einsum("bid,bjd->bij", qm, km)
+    p = scipy.special.softmax(s, axis=-1)
+    tb = (text_tokens + block - 1) // block
+    idx = np.arange(nb)
+    forced = (idx[:, None] == idx[None, :]) | (idx[:, None] < tb) | (idx[None, :] < tb)
+    mask = ((p >= tau / nb) | forced[None]).astype(np.uint8)
+    return mask.reshape(B, H, nb, nb), p.reshape(B, H, nb, nb)
+
+
+@pytest.mark.parametrize("N,tau,text", [(640, 1.0, 128), (700, 1.05, 0), (1000, 1.6, 64)])
+def test_select_blocks_vs_library_pooling_and_softmax(N, tau, text):
+    g = torch.Generator().manual_seed(200 + N)
+    q, k = (torch.randn((1, 2, N, 128), generator=g) * 3).to(torch.bfloat16), \
+        (torch.randn((1, 2, N, 128), generator=g) * 3).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(128)
+    mask, share = oracle.select_blocks(q, k, scale, tau, text)
+    ref_mask, ref_share = _library_select(q, k, scale, tau, text)
+    assert np.max(np.abs(share - ref_share)) <= 1e-13
+    assert np.allclose(share.sum(-1), 1.0, atol=1e-13)
+    near = np.abs(ref_share - tau / ref_share.shape[-1]) <= 1e-9 * tau / ref_share.shape[-1]
+    assert np.array_equal(mask[~near], ref_mask[~near])
+    # the rule thins: fewer kept blocks than the dense count, more than the forced ones
+    assert 0 < int(mask.sum()) < mask.size
+
+
+def test_select_blocks_invariants():
+    """Shifting every key by one vector shifts a row's logits by a constant
+    (softmax unchanged); permuting whole key blocks permutes the shares'
+    columns; tau = 0 keeps everything."""
+    N, scale = 768, 1.0 / math.sqrt(128)
+    g = torch.Generator().manual_seed(210)
+    q = (torch.randn((1, 1, N, 128), generator=g) * 2).to(torch.bfloat16)
+    k = (torch.randn((1, 1, N, 128), generator=g) * 2).to(torch.bfloat16)
+    _, share = oracle.select_blocks(q, k, scale, 1.0, 0)
+    shift = torch.randn(128, generator=g).to(torch.bfloat16)
+    _, share_s = oracle.select_blocks(q, (k.double() + shift.double()), scale, 1.0, 0)
+    assert np.max(np.abs(share - share_s)) <= 1e-12
+    perm = torch.tensor([3, 0, 5, 1, 4, 2])
+    kp = k.reshape(1, 1, 6, 128, 128)[:, :, perm].reshape(1, 1, N, 128)
+    _, share_p = oracle.select_blocks(q, kp, scale, 1.0, 0)
+    assert np.max(np.abs(share_p - share[..., perm.numpy()])) <= 1e-13
+    mask0, _ = oracle.select_blocks(q, k, scale, 0.0, 0)
+    assert mask0.all()
+
+
+def test_select_blocks_identical_key_blocks_and_planted_block():
+    """Every key block with the same mean: every share is exactly 1 / nb, so
+    tau just below 1 keeps everything and just above keeps only the forced
+    blocks.  A key block aligned with a query block's mean takes almost all
+    of its mass and is the only unforced block kept at tau = 1."""
+    nb, scale = 5, 1.0 / math.sqrt(128)
+    g = torch.Generator().manual_seed(220)
+    q = torch.randn((1, 1, nb * 128, 128), generator=g).to(torch.bfloat16)
+    blockk = torch.randn((1, 1, 128, 128), generator=g).to(torch.bfloat16)
+    k = blockk.repeat(1, 1, nb, 1)
+    m_lo, share = oracle.select_blocks(q, k, scale, 0.999, 0)
+    assert np.array_equal(share, np.full_like(share, 1.0 / nb))
+    assert m_lo.all()
+    m_hi, _ = oracle.select_blocks(q, k, scale, 1.001, 128)
+    idx = np.arange(nb)
+    forced = (idx[:, None] == idx[None, :]) | (idx[:, None] < 1) | (idx[None, :] < 1)
+    assert np.array_equal(m_hi[0, 0], forced.astype(np.uint8))
+    # planted: key block 3 = 20 x the mean of query block 1, tokens otherwise noise
+    k2 = (torch.randn((1, 1, nb * 128, 128), generator=g) * 0.1).to(torch.bfloat16)
+    qmean = q[0, 0, 128:256].double().mean(0)
+    k2[0, 0, 384:512] = (20 * qmean).to(torch.bfloat16)
+    m2, share2 = oracle.select_blocks(q, k2, scale, 1.0, 0)
+    assert share2[0, 0, 1, 3] > 0.5
+    kept_unforced = [j for j in range(nb) if m2[0, 0, 1, j] and j != 1]
+    assert kept_unforced == [3]
