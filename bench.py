@@ -14,7 +14,9 @@ already resident in HBM).  `value` is the algorithmic TFLOP/s of that step
 In the same run and on the same stream, timed the same way (W warm-ups, then
 K timed launches between HIP events), the other configurations are reported
 as legs: the fp8 recipe (quantisation pass + fp8 attention) and the
-block-sparse kernel at the 2048^2 shape with B=1, the dense kernel at the
+block-sparse kernel at the 2048^2 shape with B=1, the block-mask selection
+(tau = 1, on inputs with spatial locality) and block-sparse attention on the
+mask it selects at that shape, the dense kernel at the
 1024^2 shape and on the image-to-image joint sequence, and the tiny shape
 (launch-bound: its time per launch comes from a HIP graph of many launches,
 so host-side call overhead is not counted).  For the step, launch_stats adds
@@ -193,7 +195,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--legs", default="all", choices=["all", "none"],
-                    help="also time the fp8, block-sparse, 1024^2, image-to-image and tiny legs")
+                    help="also time the fp8, block-sparse, mask-selection, 1024^2, image-to-image "
+                         "and tiny legs")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one device-to-device copy of MIB MiB (a kernel of "
                          "known traffic, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -207,7 +210,7 @@ def main():
     import torch
 
     import joint_attention_non_amd as dit
-    from workloads import WORKLOADS, block_rows, make_workload_inputs
+    from workloads import WORKLOADS, block_rows, make_local_qkv, make_workload_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -307,6 +310,40 @@ def main():
                           "flops_counted": "active 128x128 blocks only"}
         log(f"[bench] {wsp.name}: {legs[wsp.name]}")
         del qs, ks, vs, md, os_
+
+        # mask selection at 2048^2, B=1 (tau = 1, inputs with spatial locality),
+        # then block-sparse attention on the selected mask
+        log("[bench] leg img2048_select")
+        qs, ks, vs = (t.to(dev) for t in make_local_qkv(wsp.batch, wsp.heads, wsp.seqlen,
+                                                         wsp.text_tokens, seed=0))
+        nbs = (wsp.seqlen + 127) // 128
+        msel = torch.empty((wsp.batch, wsp.heads, nbs, nbs), dtype=torch.uint8, device=dev)
+        wsel = torch.empty(dit.select_blocks_workspace_bytes(qs), dtype=torch.uint8, device=dev)
+        os_ = torch.empty_like(qs)
+        ms_sel = _time_launches(lambda: dit.select_blocks(qs, ks, 1.0, wsp.text_tokens, out=msel,
+                                                          workspace=wsel),
+                                max(args.steps, 50), args.warmup, torch)
+        active = int(msel.sum())
+        ms_ss = _time_launches(lambda: dit.attn_fwd_blocksparse(qs, ks, vs, msel, out=os_),
+                               args.steps, args.warmup, torch)
+        fs = 4.0 * active * 128 * 128 * wsp.head_dim
+        sel_bytes = 2 * qs.numel() * 2 + msel.numel()      # Q, K read once; mask written
+        legs["img2048_select"] = {
+            "tau": 1.0, "inputs": "make_local_qkv (amp 16, length 8), seed 0",
+            "ms_select": round(ms_sel, 4), "active_blocks": active, "total_blocks": int(msel.numel()),
+            "density": round(active / msel.numel(), 4),
+            "select": {"bound": "hbm", "achieved": round(sel_bytes / (ms_sel * 1e-3) / 1e9, 1),
+                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": round(sel_bytes / (ms_sel * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "bytes_per_launch": sel_bytes},
+            "ms_sparse_attention": round(ms_ss, 4),
+            "sparse_attention": {"bound": "mfma", "achieved": round(fs / (ms_ss * 1e-3) / 1e12, 2),
+                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(fs / (ms_ss * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "ms_select_plus_attention": round(ms_sel + ms_ss, 4),
+        }
+        log(f"[bench] img2048_select: {legs['img2048_select']}")
+        del qs, ks, vs, msel, wsel, os_
 
         for wname in ("img1024", "i2i2048"):
             w1 = WORKLOADS[wname]

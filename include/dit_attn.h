@@ -211,6 +211,41 @@ int dit_attn_fwd_blocksparse(const dit_attn_shape* shape,
                              int32_t block_size,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes dit_attn_select_blocks needs for `shape`: the fp32
+ * block means of Q and K, 2 * B * H * ceil(N/128) * 128 * 4 bytes. */
+size_t dit_attn_select_blocks_workspace_bytes(const dit_attn_shape* shape);
+
+/* Block-mask selection for dit_attn_fwd_blocksparse, in the manner of
+ * Sol-Attention (a block-sparse backend whose sparsity a threshold tau
+ * controls: bpdata.com page, section "Részletes optimalizációs lépések és
+ * hatásuk").  The pages give no rule; the one built here estimates, for each
+ * (b, h) and query block i, the share of attention each key block j draws,
+ * from block-mean-pooled queries and keys:
+ *     qm_i, km_j = means of q, k over the valid tokens of 128-token blocks
+ *     s_ij = softmax_scale * <qm_i, km_j>,   p_ij = softmax over j of s_ij
+ * and keeps block j iff p_ij >= tau / nb (at least tau times the uniform
+ * share), or j == i, or i < tb, or j < tb, with nb = ceil(N/128) and
+ * tb = ceil(text_tokens/128): the diagonal and the rows and columns of the
+ * text blocks (the first text_tokens tokens of the joint sequence) are
+ * always kept.  tau = 0 keeps every block; larger tau keeps fewer.
+ * Reads q and k ([B, H, N, 128] bf16, strides from `shape`; v, o, lse and
+ * the flags are not used) and writes block_mask, a device uint8 array
+ * [B*H][nb][nb] (b-major, row = query block, 1 = keep), ready for
+ * dit_attn_fwd_blocksparse with mask_stride_bh = nb * nb.  The shares are
+ * computed in fp32 with fixed-order reductions, so a call is deterministic;
+ * a share within about 1e-5 relative of tau / nb may be decided either way
+ * compared with exact arithmetic.
+ * tau must be finite and >= 0, text_tokens in [0, N], nb <= 4096
+ * (ERR_UNSUPPORTED beyond).  workspace: device memory of at least
+ * dit_attn_select_blocks_workspace_bytes(shape) bytes, 256-byte aligned
+ * (ERR_WORKSPACE otherwise), overwritten.  Two kernels run on `stream`; the
+ * mask is ready when the stream reaches that point. */
+int dit_attn_select_blocks(const dit_attn_shape* shape,
+                           const void* q, const void* k,
+                           float tau, int32_t text_tokens,
+                           uint8_t* block_mask,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* dit_attn_status_string(int status);
 

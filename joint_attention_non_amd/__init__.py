@@ -10,6 +10,7 @@ call fails, an exception is raised.
     attn_fwd_blocksparse(q, k, v, block_mask, scale=None, return_lse=False, out_fp32=False, out=None,
                          workspace=None, lse_out=None)
     fp8_quantize(q, k, v, workspace=None) -> Fp8Workspace views
+    select_blocks(q, k, tau, text_tokens, scale=None, out=None, workspace=None) -> uint8 [B, H, nb, nb]
 
 q, k, v: CUDA (HIP) bfloat16 tensors [B, H, N, 128] whose last dimension is
 contiguous (any other strides that are multiples of 8 elements).
@@ -25,7 +26,8 @@ import torch
 
 __all__ = ["attn_fwd", "attn_fwd_fp8", "attn_fwd_blocksparse", "fp8_quantize",
            "fp8_workspace_bytes", "fwd_workspace_bytes", "fwd_workspace",
-           "blocksparse_workspace_bytes", "attn_fwd_noalloc", "DitAttnError",
+           "blocksparse_workspace_bytes", "attn_fwd_noalloc", "select_blocks",
+           "select_blocks_workspace_bytes", "DitAttnError",
            "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,6 +85,11 @@ def load():
         lib.dit_attn_fwd_blocksparse.argtypes = [sp, vp, vp, vp, vp, vp, vp, ctypes.c_int64,
                                                  ctypes.c_int32, vp, ctypes.c_size_t, vp]
         lib.dit_attn_fwd_blocksparse.restype = ctypes.c_int
+        lib.dit_attn_select_blocks_workspace_bytes.argtypes = [sp]
+        lib.dit_attn_select_blocks_workspace_bytes.restype = ctypes.c_size_t
+        lib.dit_attn_select_blocks.argtypes = [sp, vp, vp, ctypes.c_float, ctypes.c_int32, vp, vp,
+                                               ctypes.c_size_t, vp]
+        lib.dit_attn_select_blocks.restype = ctypes.c_int
         lib.dit_attn_status_string.argtypes = [ctypes.c_int]
         lib.dit_attn_status_string.restype = ctypes.c_char_p
         lib.dit_attn_last_error.argtypes = []
@@ -267,6 +274,37 @@ def attn_fwd_blocksparse(q, k, v, block_mask, scale=None, return_lse=False, out_
                                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                            _stream()), "dit_attn_fwd_blocksparse")
     return _ret(o, lse, return_lse)
+
+
+def select_blocks_workspace_bytes(q) -> int:
+    """Bytes of workspace dit_attn_select_blocks needs for q's shape."""
+    B, H, N, D = q.shape
+    s = _Shape()
+    s.batch, s.heads, s.seqlen, s.head_dim = B, H, N, D
+    return int(load().dit_attn_select_blocks_workspace_bytes(ctypes.byref(s)))
+
+
+def select_blocks(q, k, tau, text_tokens, scale=None, out=None, workspace=None):
+    """Block-mask selection (dit_attn_select_blocks): returns a uint8 device
+    tensor [B, H, nb, nb] (1 = keep) that attn_fwd_blocksparse takes as is.
+    `out`, when given, must be a contiguous uint8 tensor of that shape."""
+    _check_inputs(q, k, k)
+    B, H, N, D = q.shape
+    nb = (N + 127) // 128
+    if out is None:
+        out = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=q.device)
+    elif (not isinstance(out, torch.Tensor) or not out.is_cuda or out.device != q.device
+          or out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() != B * H * nb * nb):
+        raise ValueError(f"out must be a contiguous uint8 device tensor of {B * H * nb * nb} elements")
+    need = select_blocks_workspace_bytes(q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q)
+    s = _shape(q, k, k, q, scale, 0)
+    _check(load().dit_attn_select_blocks(ctypes.byref(s), _ptr(q), _ptr(k), float(tau), int(text_tokens),
+                                         _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
+           "dit_attn_select_blocks")
+    return out
 
 
 def fp8_workspace_bytes(q) -> int:

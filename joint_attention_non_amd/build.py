@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdit_attn.so")
-SOURCES = ["attn_bf16.hip", "attn_fp8.hip", "dit_attn_api.cpp"]
+SOURCES = ["attn_bf16.hip", "attn_fp8.hip", "select_blocks.hip", "dit_attn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -398,6 +398,59 @@ int dit_attn_fwd_fp8(const dit_attn_shape* shape, const void* q, const void* k, 
   return hip_status(dit::launch_attn_fp8(f, (shape->flags & DIT_ATTN_FLAG_OUT_F32) != 0, s), "fp8 attention launch");
 }
 
+size_t dit_attn_select_blocks_workspace_bytes(const dit_attn_shape* shape) {
+  if (shape == nullptr || shape->batch < 1 || shape->heads < 1 || shape->seqlen < 1) return 0;
+  const int64_t nb = (shape->seqlen + 127) / 128;
+  return (size_t)(2 * (int64_t)shape->batch * shape->heads * nb * 128 * 4);
+}
+
+int dit_attn_select_blocks(const dit_attn_shape* shape, const void* q, const void* k, float tau,
+                           int32_t text_tokens, uint8_t* block_mask, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  g_err[0] = '\0';
+  if (shape == nullptr) return fail(DIT_ATTN_ERR_INVALID_ARG, "shape is NULL");
+  // Only q and k are read: validate them with the common checks (v and o
+  // stand in as q, with q's strides).
+  dit_attn_shape tmp = *shape;
+  for (int i = 0; i < 3; ++i) tmp.v_stride[i] = tmp.o_stride[i] = tmp.q_stride[i];
+  tmp.flags = 0;
+  int rc = check_common(&tmp, q, k, q, q, nullptr);
+  if (rc) return rc;
+  if (!(std::isfinite(tau) && tau >= 0.f)) return fail(DIT_ATTN_ERR_INVALID_ARG, "tau must be finite and >= 0");
+  if (text_tokens < 0 || text_tokens > shape->seqlen)
+    return fail(DIT_ATTN_ERR_INVALID_ARG, "text_tokens=%d is outside [0, seqlen=%d]", text_tokens, shape->seqlen);
+  if (block_mask == nullptr) return fail(DIT_ATTN_ERR_INVALID_ARG, "block_mask is NULL");
+  const int64_t nb = (shape->seqlen + 127) / 128;
+  if (nb > dit::kSelectMaxBlocks)
+    return fail(DIT_ATTN_ERR_UNSUPPORTED, "seqlen=%d: the selection kernel handles at most %d blocks",
+                shape->seqlen, dit::kSelectMaxBlocks);
+  const size_t need = dit_attn_select_blocks_workspace_bytes(shape);
+  if (workspace == nullptr) return fail(DIT_ATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned(workspace, 256)) return fail(DIT_ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(DIT_ATTN_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, need);
+  dit::SelectArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = shape->q_stride[i];
+    a.ks[i] = shape->k_stride[i];
+  }
+  a.q_bytes = (uint32_t)slice_bytes(shape->seqlen, shape->q_stride[2], 2);
+  a.k_bytes = (uint32_t)slice_bytes(shape->seqlen, shape->k_stride[2], 2);
+  a.B = shape->batch;
+  a.H = shape->heads;
+  a.N = shape->seqlen;
+  a.nb = (int)nb;
+  a.tb = (text_tokens + 127) / 128;
+  a.scale = shape->softmax_scale;
+  a.tau = tau;
+  a.pooled = static_cast<float*>(workspace);
+  a.mask = block_mask;
+  return hip_status(dit::launch_select_blocks(a, static_cast<hipStream_t>(stream)), "dit_attn_select_blocks launch");
+}
+
 const char* dit_attn_status_string(int status) {
   switch (status) {
     case DIT_ATTN_OK: return "ok";

@@ -64,6 +64,18 @@ struct Fp8Args {
   float* part;          // [ntail * split][bm rows][kPartRow] fp32
 };
 
+// Arguments of the block-mask selection passes.
+struct SelectArgs {
+  const void* q;
+  const void* k;
+  int64_t qs[3], ks[3];
+  uint32_t q_bytes, k_bytes;
+  int B, H, N, nb, tb;           // nb = ceil(N / 128), tb = ceil(text tokens / 128)
+  float scale, tau;
+  float* pooled;                 // fp32 block means: Q [BH][nb][128], then K transposed [BH][128][nb]
+  uint8_t* mask;                 // [BH][nb][nb]
+};
+
 // Launch `kernel` and return the status of this launch alone: hipLaunchKernel
 // reports it directly, whereas hipGetLastError would also return (and clear)
 // an error left on the thread by an earlier, unrelated HIP call.
@@ -77,5 +89,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, bool out_f32, bool sparse, hipStr
 hipError_t launch_attn_merge(const AttnArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_fp8_quantize(const Fp8Args& a, hipStream_t s);
 hipError_t launch_attn_fp8(const Fp8Args& a, bool out_f32, hipStream_t s);
+hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t s);
+constexpr int kSelectMaxBlocks = 4096;   // nb limit of the selection kernel (key-block logits kept in registers)
 
 }  // namespace dit

@@ -28,7 +28,8 @@ def test_header_declares_the_expected_calls():
               "dit_attn_fwd_fp8", "dit_attn_fwd_fp8_workspace_bytes",
               "dit_attn_fp8_quantize", "dit_attn_fwd_blocksparse",
               "dit_attn_fwd_blocksparse_workspace_bytes", "dit_attn_fwd_noalloc",
-              "dit_attn_fwd_noalloc_scratch_bytes", "dit_attn_status_string",
+              "dit_attn_fwd_noalloc_scratch_bytes", "dit_attn_select_blocks",
+              "dit_attn_select_blocks_workspace_bytes", "dit_attn_status_string",
               "dit_attn_last_error", "dit_attn_version"):
         assert n in names
 
@@ -197,6 +198,38 @@ def test_noalloc_checks_arguments_before_any_device_call():
     assert lib.dit_attn_fwd_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None, None) == UNSUPPORTED
     assert lib.dit_attn_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
     assert lib.dit_attn_fwd_noalloc(ctypes.byref(_shape()), FAKE, None, FAKE, FAKE, None, None) == INVALID
+
+
+def test_select_blocks_checks_arguments_before_any_device_call():
+    lib = dit.load()
+    s = _shape(B=1, H=2, N=320)
+    need = lib.dit_attn_select_blocks_workspace_bytes(ctypes.byref(s))
+    assert need == 2 * 2 * 3 * 128 * 4          # fp32 block means of Q and K
+    assert lib.dit_attn_select_blocks_workspace_bytes(None) == 0
+    f = lib.dit_attn_select_blocks
+    assert f(ctypes.byref(s), FAKE, FAKE, 1.0, 0, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert f(ctypes.byref(s), FAKE, FAKE, 1.0, 0, FAKE, None, need, None) == WORKSPACE
+    assert f(ctypes.byref(s), FAKE, FAKE, 1.0, 0, FAKE, FAKE + 16, need, None) == WORKSPACE
+    assert f(ctypes.byref(s), FAKE, FAKE, 1.0, 0, None, FAKE, need, None) == INVALID       # no mask
+    assert f(ctypes.byref(s), FAKE, None, 1.0, 0, FAKE, FAKE, need, None) == INVALID       # no k
+    assert f(ctypes.byref(s), FAKE, FAKE, -0.5, 0, FAKE, FAKE, need, None) == INVALID      # tau < 0
+    assert f(ctypes.byref(s), FAKE, FAKE, float("nan"), 0, FAKE, FAKE, need, None) == INVALID
+    assert f(ctypes.byref(s), FAKE, FAKE, float("inf"), 0, FAKE, FAKE, need, None) == INVALID
+    assert f(ctypes.byref(s), FAKE, FAKE, 1.0, -1, FAKE, FAKE, need, None) == INVALID      # text < 0
+    assert f(ctypes.byref(s), FAKE, FAKE, 1.0, 321, FAKE, FAKE, need, None) == INVALID     # text > N
+    assert f(None, FAKE, FAKE, 1.0, 0, FAKE, FAKE, need, None) == INVALID
+    big = _shape(B=1, H=1, N=4097 * 128)       # 4097 blocks: beyond the selection kernel
+    nbig = lib.dit_attn_select_blocks_workspace_bytes(ctypes.byref(big))
+    assert f(ctypes.byref(big), FAKE, FAKE, 1.0, 0, FAKE, FAKE, nbig, None) == UNSUPPORTED
+    assert "4096" in lib.dit_attn_last_error().decode()
+
+
+def test_binding_select_blocks_rejects_bad_out():
+    q, k, _ = _qkv()
+    with pytest.raises(ValueError, match="out"):
+        dit.select_blocks(q, k, 1.0, 0, out=_dev(torch.zeros((1, 2, 3, 2), dtype=torch.uint8)))
+    with pytest.raises(ValueError, match="out"):
+        dit.select_blocks(q, k, 1.0, 0, out=_dev(torch.zeros((1, 2, 3, 3), dtype=torch.int32)))
 
 
 def test_status_strings():

@@ -39,7 +39,7 @@ def test_random_mask_full_parity(N):
 
 
 def test_all_ones_mask_equals_dense():
-    """Every block kept: the sparse kernel (64-key tiles, 128-row blocks) and
+    """Every block kept: the sparse kernel (32-key tiles, 128-row blocks) and
     the dense one (32-key tiles, 384-row blocks) compute the same attention;
     both meet the oracle gates and agree with each other within them."""
     _say("case: all-ones mask vs dense")

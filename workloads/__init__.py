@@ -112,6 +112,34 @@ def make_qkv(B: int, H: int, N: int, D: int = HEAD_DIM, seed: int = 0,
     return q.contiguous(), k.contiguous(), v.contiguous()
 
 
+def make_local_qkv(B: int, H: int, N: int, text_tokens: int, D: int = HEAD_DIM, seed: int = 0,
+                   amp: float = 16.0, length: float = 8.0):
+    """(q, k, v) like ``make_qkv`` whose image tokens also carry a shared
+    positional feature, so that tokens near each other on the latent grid
+    have correlated queries and keys (the locality that block-sparse
+    attention exploits).  Image token t sits at (t // side, t % side) of a
+    grid of width side = ceil(sqrt(N - text_tokens)); per head h the feature
+    is sqrt(2 / D) cos(<omega_h,d, pos> + phase_h,d) over d (random Fourier
+    features: omega ~ N(0, I / length^2), phase ~ U[0, 2 pi), drawn from
+    ``manual_seed(seed + 4)`` in that order), scaled by ``amp`` and added in
+    float32 to the Gaussian q and k before the bfloat16 rounding.  Text
+    tokens and v are unchanged."""
+    g = torch.Generator().manual_seed(seed)
+    q, k, v = (torch.randn((B, H, N, D), generator=g) for _ in range(3))
+    n_img = N - text_tokens
+    if n_img > 0:
+        side = math.ceil(math.sqrt(n_img))
+        t = torch.arange(n_img)
+        pos = torch.stack([(t // side).float(), (t % side).float()], dim=1)        # [n_img, 2]
+        gf = torch.Generator().manual_seed(seed + 4)
+        omega = torch.randn((H, D, 2), generator=gf) / length
+        phase = torch.rand((H, D), generator=gf) * (2 * math.pi)
+        feat = math.sqrt(2.0 / D) * torch.cos(torch.einsum("pc,hdc->hpd", pos, omega) + phase[:, None, :])
+        q[:, :, text_tokens:, :] += amp * feat[None]
+        k[:, :, text_tokens:, :] += amp * feat[None]
+    return tuple(t.to(torch.bfloat16).contiguous() for t in (q, k, v))
+
+
 def peaked_key_rows(N: int, seed: int = 0, frac: float = 0.01) -> torch.Tensor:
     n_peak = int(math.floor(frac * N))
     return torch.randperm(N, generator=torch.Generator().manual_seed(seed + 1))[:n_peak]
