@@ -89,7 +89,7 @@ constexpr float kEndCheck = 0x1p80f;
 // and sum take two exchanges (lanes l^16, then l^32).
 
 constexpr int RBN = 32;                 // keys per tile
-constexpr int RNB = 3;                  // LDS tile buffers
+constexpr int RNB = 4;                  // LDS tile buffers
 constexpr int RRB = 3;                  // 16-row blocks per wave
 constexpr int RNW = 8;                  // waves per work-group
 constexpr int RBM = RNW * 16 * RRB;     // 384 query rows per work-group
@@ -101,44 +101,85 @@ constexpr int RNT = RNW * 64;
 // bank-conflict cycles of 64-bank strides of 68, 76, 80, 84 or 92 (88 ties).
 constexpr int RVS = D + 16;
 
-// Global -> register -> LDS staging of one 32-key tile of K and V (row-major,
-// padded rows), as 16-byte chunks: 32 keys x 16 chunks per tensor, CH of
-// them per thread; chunk J < CH is K, the rest V.
-template <int NT>
-struct RLoader {
-  static constexpr int CH = RBN * 16 / NT;
-  static_assert(CH * NT == RBN * 16, "tile split");
-  u32x4 r[2 * CH];
-  template <int J>
-  __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t krow,
-                                           uint32_t vrow, int key0, int N, int tid) {
-    constexpr bool isk = J < CH;
-    const int cid = tid + (J % CH) * NT, key = cid >> 4, c = cid & 15;
-    const int row = min(key0 + key, N);
-    r[J] = buf_load_b128(isk ? rk : rv, (uint32_t)row * (isk ? krow : vrow) + c * 16);
-  }
-  template <int J>
-  __device__ __forceinline__ void store_one(__bf16* sk, __bf16* sv, int tid) const {
-    constexpr bool isk = J < CH;
-    const int cid = tid + (J % CH) * NT, key = cid >> 4, c = cid & 15;
-    *reinterpret_cast<u32x4*>((isk ? sk + key * KS : sv + key * RVS) + c * 8) = r[J];
-  }
-  template <int J = 0>
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t krow,
-                                       uint32_t vrow, int key0, int N, int tid) {
-    if constexpr (J < 2 * CH) {
-      load_one<J>(rk, rv, krow, vrow, key0, N, tid);
-      load<J + 1>(rk, rv, krow, vrow, key0, N, tid);
+// Direct global -> LDS staging of one 32-key tile (buffer_load ... lds): a
+// tile buffer holds the 32 K rows at the 272-byte stride and the 32 V rows
+// at 288 bytes, each in a region of 576 16-byte slots, then a 1 KB junk
+// area.  One such instruction writes 64 consecutive slots (lane i -> slot
+// i), so a region takes 9 instructions and a tile 18.  They are dealt to the
+// waves round-robin (instruction i to wave i % NW); the PER * NW - 18 left
+// over load into the junk area, so that every wave issues exactly PER per
+// tile.  A slot in a row's padding or past the 32 K rows gets some chunk of
+// row 31 of the tile: those slots are never read.  Rows at or past N lie
+// beyond the buffer resource and load zeros.
+constexpr int kRegion = 576 * 8;               // bf16 per tensor region (9216 B)
+constexpr int kTileBuf = 2 * kRegion + 512;    // bf16 per tile buffer: K, V, junk
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <int NW>
+struct TileDma {
+  static constexpr int NI = 18;
+  static constexpr int PER = (NI + NW - 1) / NW;
+  uint32_t off[PER];    // this lane's byte offset inside the tile, per instruction
+  i32x4 rsrc[PER];      // buffer resource (K or V slice), wave-uniform
+  uint32_t dst[PER];    // LDS byte offset inside a tile buffer, wave-uniform
+  uint32_t srow[PER];   // row stride in bytes of that tensor, wave-uniform
+  __device__ __forceinline__ void init(int wave, int lane, const void* kp, uint32_t kbytes, uint32_t krow,
+                                       const void* vp, uint32_t vbytes, uint32_t vrow) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = wave + j * NW;
+      const bool isv = i >= NI / 2;
+      const int slot = 64 * (isv ? i - NI / 2 : i) + lane;
+      const int per_row = isv ? RVS / 8 : KS / 8;   // 18 or 17 slots
+      const int row = min(slot / per_row, RBN - 1), c = min(slot % per_row, 15);
+      const uint32_t rstride = isv ? vrow : krow;
+      off[j] = (uint32_t)row * rstride + 16u * (uint32_t)c;
+      const uint64_t base = reinterpret_cast<uint64_t>(isv ? vp : kp);
+      rsrc[j] = i32x4{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)(isv ? vbytes : kbytes),
+                      0x00020000};
+      dst[j] = i >= NI ? 2u * 2u * kRegion : 2u * (uint32_t)(isv ? kRegion + 512 * (i - NI / 2) : 512 * i);
+      srow[j] = rstride;
     }
   }
+  // Instruction J of this wave for the tile whose first key row is `key0`,
+  // into the tile buffer at LDS byte address `buf`.  Issued from inline
+  // assembly: the compiler would otherwise order every later LDS read of
+  // the work-group after it (it cannot tell the buffers apart).  The only
+  // register it reads is the address, at issue; completion is awaited by
+  // dma_barrier / dma_wait_all.
+  template <int J>
+  __device__ __forceinline__ void issue(uint32_t buf, uint32_t key0) const {
+    const uint32_t voff = off[J] + key0 * srow[J];
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(buf + dst[J]), "v"(voff), "s"(rsrc[J])
+                 : "memory", "m0");
+  }
   template <int J = 0>
-  __device__ __forceinline__ void store(__bf16* sk, __bf16* sv, int tid) const {
-    if constexpr (J < 2 * CH) {
-      store_one<J>(sk, sv, tid);
-      store<J + 1>(sk, sv, tid);
+  __device__ __forceinline__ void issue_all(uint32_t buf, uint32_t key0) const {
+    if constexpr (J < PER) {
+      issue<J>(buf, key0);
+      issue_all<J + 1>(buf, key0);
     }
   }
 };
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
+}
+
+// The barrier after a step's MFMA stream.  Each wave first waits until at
+// most its PER newest staging loads (the tile it issued in this step) are in
+// flight: the tile issued in the step before, which the next step reads, is
+// then in LDS for every wave.  The compiler does not order these loads
+// against the barrier by itself, hence the explicit wait.
+template <int PER>
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PER) : "memory");
+}
+__device__ __forceinline__ void dma_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -175,20 +216,15 @@ __device__ __forceinline__ bf16x8 r_p_operand(const uint32_t (&pk)[4]) {
 constexpr int kRPre = 3;   // operand pairs read this many steps ahead (2-4 measured within 1 %)
 
 // Operand pair I of a step (0..15), NRB MFMAs each (row blocks), plus the
-// NRB row-sum MFMAs at I = 8.  The 2 CH staged chunks of the next tile are
-// stored to LDS and their registers refilled with the tile after it, spread
-// evenly over the PV half (I = 8, 12 for 512 threads; 8, 10, 12, 14 for 256).
-template <int NT>
-constexpr int r_stage_every() { return 8 / (2 * RLoader<NT>::CH); }
+// NRB row-sum MFMAs at I = 8.  The wave's PER staging loads of the tile
+// three ahead go out at I = 1, 3, 5, ...
 
 template <int I, int NT, int NRB>
 __device__ __forceinline__ void r_step(f32x4 (&sacc)[2][NRB], f32x4 (&oacc)[8][NRB], f32x4 (&lacc)[NRB],
                                        const bf16x8& ones, const bf16x8 (&qf)[NRB][4],
                                        const uint32_t (&pk)[NRB][4], const __bf16* sK, const __bf16* sV, int l16,
-                                       int g, int s, bf16x8 (&fr)[kRPre + 1], RLoader<NT>& ld, __bf16* sks,
-                                       __bf16* svs,
-                                       __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t krow,
-                                       uint32_t vrow, int kload, int N, int tid) {
+                                       int g, int s, bf16x8 (&fr)[kRPre + 1], const TileDma<NT / 64>& dma,
+                                       uint32_t dbuf, uint32_t dkey) {
   if constexpr (I < 16) {
     if constexpr (I + kRPre < 16) fr[(I + kRPre) % (kRPre + 1)] = r_operand<I + kRPre>(sK, sV, l16, g, s);
     const bf16x8 a = fr[I % (kRPre + 1)];
@@ -204,14 +240,10 @@ __device__ __forceinline__ void r_step(f32x4 (&sacc)[2][NRB], f32x4 (&oacc)[8][N
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) lacc[rb] = mfma16(ones, r_p_operand(pk[rb]), lacc[rb]);
       }
-      constexpr int every = r_stage_every<NT>();
-      if constexpr ((I - 8) % every == 0) {
-        ld.template store_one<(I - 8) / every>(sks, svs, tid);
-        ld.template load_one<(I - 8) / every>(rk, rv, krow, vrow, kload, N, tid);
-      }
     }
-    r_step<I + 1, NT, NRB>(sacc, oacc, lacc, ones, qf, pk, sK, sV, l16, g, s, fr, ld, sks, svs, rk, rv, krow, vrow,
-                           kload, N, tid);
+    if constexpr ((I & 1) == 1 && (I >> 1) < TileDma<NT / 64>::PER)
+      dma.template issue<(I >> 1)>(dbuf, dkey);
+    r_step<I + 1, NT, NRB>(sacc, oacc, lacc, ones, qf, pk, sK, sV, l16, g, s, fr, dma, dbuf, dkey);
   }
 }
 
@@ -220,10 +252,7 @@ __device__ __forceinline__ void r_step_schedule() {
   if constexpr (I < 16) {
     if constexpr (I + kRPre < 16) __builtin_amdgcn_sched_group_barrier(0x100, I + kRPre < 8 ? 1 : 2, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, I == 8 ? 2 * NRB : NRB, 0);
-    if constexpr (I >= 8 && (I - 8) % r_stage_every<NT>() == 0) {
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
+    if constexpr ((I & 1) == 1 && (I >> 1) < TileDma<NT / 64>::PER) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     r_step_schedule<I + 1, NT, NRB>();
   }
 }
@@ -333,8 +362,7 @@ __device__ __forceinline__ void r_prefetch(bf16x8 (&fr)[kRPre + 1], const __bf16
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 smK[RNB][RBN * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 smV[RNB][RBN * RVS];
+  __shared__ __attribute__((aligned(16))) __bf16 smT[RNB][kTileBuf];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4, s = lane & 15;
@@ -355,8 +383,6 @@ __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
   const __bf16* kp = static_cast<const __bf16*>(a.k) + b * a.ks[0] + hd * a.ks[1];
   const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.vs[0] + hd * a.vs[1];
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qp, a.q_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, a.k_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, a.v_bytes);
   const uint32_t qrow = (uint32_t)(a.qs[2] * 2), krow = (uint32_t)(a.ks[2] * 2),
                  vrow = (uint32_t)(a.vs[2] * 2);
 
@@ -383,6 +409,9 @@ __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
   const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+  TileDma<RNW> dma;
+  dma.init(__builtin_amdgcn_readfirstlane(wave), lane, kp, a.k_bytes, krow, vp, a.v_bytes, vrow);
+  constexpr int PER = TileDma<RNW>::PER;
 
   f32x4 oacc[8][RRB];
   f32x4 lacc[RRB];   // row sums of the rounded P (every element of a row block's C holds its row's sum)
@@ -413,26 +442,24 @@ __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
       for (int r = 0; r < 4; ++r) lacc[rb][r] = 0.f;
     }
 
-    // ---- prologue: tiles t0 and t0+1 into LDS, t0+2 into registers ----
-    RLoader<RNT> ld;
-    ld.load(rk, rv, krow, vrow, t0 * RBN, N, tid);
-    ld.store(smK[0], smV[0], tid);
-    ld.load(rk, rv, krow, vrow, (t0 + 1) * RBN, N, tid);
-    ld.store(smK[1], smV[1], tid);
-    ld.load(rk, rv, krow, vrow, (t0 + 2) * RBN, N, tid);
+    // ---- prologue: tiles t0 .. t0+2 into LDS buffers 0 .. 2 ----
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dma.issue_all(lds_addr(smT[j]), (uint32_t)((t0 + j) * RBN));
+    dma_wait_all();
     __syncthreads();
 
     f32x4 sacc[2][RRB];
     uint32_t pk[RRB][4];
-    r_qk_tile(sacc, smK[0], qf, l16, g);
+    r_qk_tile(sacc, smT[0], qf, l16, g);
     if ((t0 + 1) * RBN > N) r_mask(sacc, t0 * RBN, N, g);
     r_softmax(sacc, st, oacc, lacc, pk, c, true);
 
     if (grp == 1) __syncthreads();
     bc = 0;
     for (int t = t0; t + 1 < t1; ++t) {
-      const int bn = (bc + 1 == RNB) ? 0 : bc + 1;
-      const int bn2 = (bn + 1 == RNB) ? 0 : bn + 1;
+      const int bn = (bc + 1) & (RNB - 1);
+      const int b3 = (bc + 3) & (RNB - 1);
+      const uint32_t kload = (uint32_t)((t + 3) * RBN);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -440,23 +467,24 @@ __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sacc[kb][rb][r] = 0.f;
       bf16x8 fr[kRPre + 1];
-      r_prefetch<0, kRPre>(fr, smK[bn], smV[bc], l16, g, s);
-      r_step<0, RNT, RRB>(sacc, oacc, lacc, ones, qf, pk, smK[bn], smV[bc], l16, g, s, fr, ld, smK[bn2], smV[bn2],
-                          rk, rv, krow, vrow, (t + 3) * RBN, N, tid);
+      r_prefetch<0, kRPre>(fr, smT[bn], smT[bc] + kRegion, l16, g, s);
+      r_step<0, RNT, RRB>(sacc, oacc, lacc, ones, qf, pk, smT[bn], smT[bc] + kRegion, l16, g, s, fr, dma,
+                          lds_addr(smT[b3]), kload);
       __builtin_amdgcn_sched_group_barrier(0x100, kRPre, 0);
       r_step_schedule<0, RNT, RRB>();
-      __syncthreads();
+      dma_barrier<PER>();
       const int key1 = (t + 1) * RBN;
       if (key1 + RBN > N) r_mask(sacc, key1, N, g);
       r_softmax(sacc, st, oacc, lacc, pk, c, EXACT);
-      __syncthreads();
+      plain_barrier();
       bc = bn;
     }
+    dma_wait_all();
     if (grp == 0) __syncthreads();
     // ---- drain: PV of the last tile ----
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const bf16x8 vf = r_v_operand(smV[bc], db, g, s);
+      const bf16x8 vf = r_v_operand(smT[bc] + kRegion, db, g, s);
 #pragma unroll
       for (int rb = 0; rb < RRB; ++rb) oacc[db][rb] = mfma16(vf, r_p_operand(pk[rb]), oacc[db][rb]);
     }
@@ -566,8 +594,7 @@ static_assert(SNW * 16 * SRB == kBlock, "a block-sparse work-group covers one 12
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(SNT, 2) void attn_sparse_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 smK[RNB][RBN * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 smV[RNB][RBN * RVS];
+  __shared__ __attribute__((aligned(16))) __bf16 smT[RNB][kTileBuf];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4, s = lane & 15;
@@ -581,8 +608,6 @@ __global__ __launch_bounds__(SNT, 2) void attn_sparse_kernel(AttnArgs a) {
   const __bf16* kp = static_cast<const __bf16*>(a.k) + b * a.ks[0] + hd * a.ks[1];
   const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.vs[0] + hd * a.vs[1];
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qp, a.q_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, a.k_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, a.v_bytes);
   const uint32_t qrow = (uint32_t)(a.qs[2] * 2), krow = (uint32_t)(a.ks[2] * 2),
                  vrow = (uint32_t)(a.vs[2] * 2);
   const uint8_t* mrow = a.mask + (int64_t)bh * a.mask_bh + (int64_t)qblk * a.nb;
@@ -598,6 +623,9 @@ __global__ __launch_bounds__(SNT, 2) void attn_sparse_kernel(AttnArgs a) {
     }
   const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+  TileDma<SNW> dma;
+  dma.init(__builtin_amdgcn_readfirstlane(wave), lane, kp, a.k_bytes, krow, vp, a.v_bytes, vrow);
+  constexpr int PER = TileDma<SNW>::PER;
 
   f32x4 oacc[8][SRB];
   f32x4 lacc[SRB];
@@ -623,27 +651,28 @@ __global__ __launch_bounds__(SNT, 2) void attn_sparse_kernel(AttnArgs a) {
     int k1 = tq.next();
     int k2 = (k1 >= 0) ? tq.next() : -1;
 
-    // ---- prologue: tiles k0 and k1 into LDS, k2 into registers (a missing
+    // ---- prologue: tiles k0, k1, k2 into LDS buffers 0 .. 2 (a missing
     // tile loads key offset N, i.e. zeros, into a buffer nobody reads) ----
-    RLoader<SNT> ld;
-    ld.load(rk, rv, krow, vrow, k0, N, tid);
-    ld.store(smK[0], smV[0], tid);
-    ld.load(rk, rv, krow, vrow, k1 >= 0 ? k1 : N, N, tid);
-    ld.store(smK[1], smV[1], tid);
-    ld.load(rk, rv, krow, vrow, k2 >= 0 ? k2 : N, N, tid);
+    {
+      const uint32_t kk[3] = {(uint32_t)k0, (uint32_t)(k1 >= 0 ? k1 : N), (uint32_t)(k2 >= 0 ? k2 : N)};
+#pragma unroll
+      for (int j = 0; j < 3; ++j) dma.issue_all(lds_addr(smT[j]), kk[j]);
+    }
+    dma_wait_all();
     __syncthreads();
 
     f32x4 sacc[2][SRB];
     uint32_t pk[SRB][4];
-    r_qk_tile(sacc, smK[0], qf, l16, g);
+    r_qk_tile(sacc, smT[0], qf, l16, g);
     if (k0 + RBN > N) r_mask(sacc, k0, N, g);
     r_softmax(sacc, st, oacc, lacc, pk, c, true);
 
     int bc = 0;
     while (k1 >= 0) {
-      const int bn = (bc + 1 == RNB) ? 0 : bc + 1;
-      const int bn2 = (bn + 1 == RNB) ? 0 : bn + 1;
+      const int bn = (bc + 1) & (RNB - 1);
+      const int b3 = (bc + 3) & (RNB - 1);
       const int k3 = (k2 >= 0) ? tq.next() : -1;
+      const uint32_t kload = (uint32_t)(k3 >= 0 ? k3 : N);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -651,22 +680,23 @@ __global__ __launch_bounds__(SNT, 2) void attn_sparse_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sacc[kb][rb][r] = 0.f;
       bf16x8 fr[kRPre + 1];
-      r_prefetch<0, kRPre>(fr, smK[bn], smV[bc], l16, g, s);
-      r_step<0, SNT, SRB>(sacc, oacc, lacc, ones, qf, pk, smK[bn], smV[bc], l16, g, s, fr, ld, smK[bn2], smV[bn2],
-                          rk, rv, krow, vrow, k3 >= 0 ? k3 : N, N, tid);
+      r_prefetch<0, kRPre>(fr, smT[bn], smT[bc] + kRegion, l16, g, s);
+      r_step<0, SNT, SRB>(sacc, oacc, lacc, ones, qf, pk, smT[bn], smT[bc] + kRegion, l16, g, s, fr, dma,
+                          lds_addr(smT[b3]), kload);
       __builtin_amdgcn_sched_group_barrier(0x100, kRPre, 0);
       r_step_schedule<0, SNT, SRB>();
-      __syncthreads();
+      dma_barrier<PER>();
       if (k1 + RBN > N) r_mask(sacc, k1, N, g);
       r_softmax(sacc, st, oacc, lacc, pk, c, EXACT);
       bc = bn;
       k1 = k2;
       k2 = k3;
     }
+    dma_wait_all();
     // ---- drain: PV of the last tile ----
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const bf16x8 vf = r_v_operand(smV[bc], db, g, s);
+      const bf16x8 vf = r_v_operand(smT[bc] + kRegion, db, g, s);
 #pragma unroll
       for (int rb = 0; rb < SRB; ++rb) oacc[db][rb] = mfma16(vf, r_p_operand(pk[rb]), oacc[db][rb]);
     }

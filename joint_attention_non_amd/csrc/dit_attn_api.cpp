@@ -36,6 +36,9 @@ int fail(int status, const char* fmt, ...) {
 
 constexpr uint32_t kKnownFlags = DIT_ATTN_FLAG_OUT_F32;
 constexpr int64_t kMaxSliceBytes = (int64_t)1 << 31;   // one (b, h) slice, 32-bit buffer offsets
+// Row strides up to 2^22 elements keep the 32-bit byte offsets of the key
+// tiles staged past the last row (up to 127 rows beyond N) from wrapping.
+constexpr int64_t kMaxRowStride = (int64_t)1 << 22;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -55,6 +58,9 @@ int check_tensor(const char* name, const void* p, const int64_t* st, int64_t N, 
   if (st[2] < 128)
     return fail(DIT_ATTN_ERR_INVALID_ARG, "%s row stride %lld is smaller than head_dim 128 (rows overlap)", name,
                 (long long)st[2]);
+  if (st[2] > kMaxRowStride)
+    return fail(DIT_ATTN_ERR_UNSUPPORTED, "%s row stride %lld is above %lld elements", name, (long long)st[2],
+                (long long)kMaxRowStride);
   if (slice_bytes(N, st[2], elem_bytes) >= kMaxSliceBytes)
     return fail(DIT_ATTN_ERR_UNSUPPORTED, "%s: one (batch, head) slice spans more than 2 GiB", name);
   (void)is_output;
