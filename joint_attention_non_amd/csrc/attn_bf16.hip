@@ -114,8 +114,6 @@ constexpr int RVS = D + 16;
 constexpr int kRegion = 576 * 8;               // bf16 per tensor region (9216 B)
 constexpr int kTileBuf = 2 * kRegion + 512;    // bf16 per tile buffer: K, V, junk
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
 template <int NW>
 struct TileDma {
   static constexpr int NI = 18;

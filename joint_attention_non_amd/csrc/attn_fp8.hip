@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(Fp8Args a) {
 
 constexpr int BN8 = 128;        // keys per tile = one scale block
 constexpr int RS8 = 128 + 16;   // LDS row stride in bytes (conflict-free 16-byte reads)
-constexpr int NB8 = 3;          // rotating LDS tile buffers
+constexpr int NB8 = 4;          // rotating LDS tile buffers
 constexpr int kPre8 = 2;        // MFMA operands read this many MFMAs ahead
 
 __device__ __forceinline__ i32x8 lds_frag8(const uint8_t* p) {
@@ -194,50 +194,85 @@ __device__ __forceinline__ i32x8 p_frag8(const uint32_t (&p8)[2][8], int s) {
                (int)p8[s][4], (int)p8[s][5], (int)p8[s][6], (int)p8[s][7]};
 }
 
-// Global -> register -> LDS staging of one 128-key tile of K8 (row-major)
-// and V8t (d-major), 16-byte chunks, KCH of each per thread.
-template <int NT>
-struct Loader8 {
-  static constexpr int KCH = BN8 * (D / 16) / NT;
-  static_assert(KCH * NT == BN8 * (D / 16), "tile split");
-  u32x4 r[2 * KCH];
-  template <int I>
-  __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int t, int np,
-                                           int tid) {
-    const int id = tid + (I % KCH) * NT, row = id >> 3, c = id & 7;
-    if constexpr (I < KCH) r[I] = buf_load_b128(rk, (uint32_t)(t * BN8 + row) * D + c * 16);
-    else r[I] = buf_load_b128(rv, (uint32_t)row * np + t * BN8 + c * 16);
-  }
-  template <int I>
-  __device__ __forceinline__ void store_one(uint8_t* sk, uint8_t* sv, int tid) const {
-    const int id = tid + (I % KCH) * NT, row = id >> 3, c = id & 7;
-    *reinterpret_cast<u32x4*>((I < KCH ? sk : sv) + row * RS8 + c * 16) = r[I];
-  }
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int t, int np, int tid) {
-    if constexpr (KCH == 2) {
-      load_one<0>(rk, rv, t, np, tid); load_one<1>(rk, rv, t, np, tid);
-      load_one<2>(rk, rv, t, np, tid); load_one<3>(rk, rv, t, np, tid);
-    } else {
-      static_assert(KCH == 2, "loader unrolled for 512 threads");
+// Direct global -> LDS staging of one 128-key tile (buffer_load ... lds): a
+// tile buffer holds the tile's 128 K8 rows and its 128 V8t rows (d-major),
+// each at the 144-byte stride in a region of 1152 16-byte slots, then a 1 KB
+// junk area.  One such instruction writes 64 consecutive slots (lane i ->
+// slot i): 18 per region, 36 per tile, dealt to the 8 waves round-robin
+// (instruction i to wave i % 8), the 4 left over loading into the junk area
+// so that every wave issues PER = 5 per tile.  A row's padding slot gets a
+// copy of its chunk 7 (never read).
+constexpr int kRegion8 = BN8 * RS8;            // bytes per tensor region (18432)
+constexpr int kTileBuf8 = 2 * kRegion8 + 1024;
+
+template <int NW>
+struct TileDma8 {
+  static constexpr int NI = 2 * kRegion8 / 1024;   // 36
+  static constexpr int PER = (NI + NW - 1) / NW;
+  uint32_t off[PER];    // this lane's byte offset inside the tile, per instruction
+  i32x4 rsrc[PER];      // K8 or V8t slice, wave-uniform
+  uint32_t dst[PER];    // LDS byte offset inside a tile buffer, wave-uniform
+  uint32_t step[PER];   // bytes between consecutive tiles in that tensor, wave-uniform
+  __device__ __forceinline__ void init(int wave, int lane, const uint8_t* k8, const uint8_t* v8, int np) {
+    const uint32_t bytes = (uint32_t)(np * D);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = wave + j * NW;
+      const bool isv = i >= NI / 2;
+      const int slot = 64 * (isv ? i - NI / 2 : i) + lane;
+      const int row = slot / (RS8 / 16), c = min(slot % (RS8 / 16), 7);
+      // K8 rows are 128 bytes apart and a tile is 128 rows; V8t rows (d)
+      // are np bytes apart and a tile is 128 bytes of each.
+      off[j] = (uint32_t)row * (isv ? (uint32_t)np : 128u) + 16u * (uint32_t)c;
+      const uint64_t base = reinterpret_cast<uint64_t>(isv ? v8 : k8);
+      rsrc[j] = i32x4{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)bytes, 0x00020000};
+      dst[j] = i >= NI ? 2u * kRegion8 : (uint32_t)(isv ? kRegion8 + 1024 * (i - NI / 2) : 1024 * i);
+      step[j] = isv ? (uint32_t)BN8 : (uint32_t)(BN8 * D);
     }
   }
-  __device__ __forceinline__ void store(uint8_t* sk, uint8_t* sv, int tid) const {
-    store_one<0>(sk, sv, tid); store_one<1>(sk, sv, tid);
-    store_one<2>(sk, sv, tid); store_one<3>(sk, sv, tid);
+  // Instruction J of this wave for tile t into the tile buffer at LDS byte
+  // address `buf` (inline assembly, for the reason given with the bf16
+  // kernels' staging: the compiler would order later LDS reads after it).
+  template <int J>
+  __device__ __forceinline__ void issue(uint32_t buf, uint32_t t) const {
+    const uint32_t voff = off[J] + t * step[J];
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(buf + dst[J]), "v"(voff), "s"(rsrc[J])
+                 : "memory", "m0");
+  }
+  template <int J = 0>
+  __device__ __forceinline__ void issue_all(uint32_t buf, uint32_t t) const {
+    if constexpr (J < PER) {
+      issue<J>(buf, t);
+      issue_all<J + 1>(buf, t);
+    }
   }
 };
+
+__device__ __forceinline__ uint32_t lds_addr8(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
+}
+
+// After a step's MFMA stream: wait until at most this wave's PER newest
+// staging loads (this step's tile) are in flight, then the barrier.
+template <int PER>
+__device__ __forceinline__ void dma8_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PER) : "memory");
+}
+__device__ __forceinline__ void dma8_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void plain_barrier8() { asm volatile("s_barrier" ::: "memory"); }
 
 // MFMA I (0..15) of a step: 0-7 QK^T of the next tile, 8-15 PV of the
 // current one (plus, at I = 8 and 12, the row-sum MFMA of that 64-key step
 // with an all-ones A operand: every row of its result is the column sum of
-// P8, so each lane gets its query row's sum).  The four staged chunks are
-// stored to LDS and refilled from memory beside the PV MFMAs.
+// P8, so each lane gets its query row's sum).  The wave's PER staging loads
+// of the tile three ahead go out at I = 1, 3, 5, ...
 template <int I, int NT>
 __device__ __forceinline__ void step8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f32x16& lacc, const i32x8 (&qf)[2],
                                       const uint32_t (&p8)[2][8], const uint8_t* sK, const uint8_t* sV, int l32,
-                                      int h, i32x8 (&fr)[kPre8 + 1], Loader8<NT>& ld, uint8_t* sks, uint8_t* svs,
-                                      __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int tload, int np,
-                                      int tid) {
+                                      int h, i32x8 (&fr)[kPre8 + 1], const TileDma8<NT / 64>& dma, uint32_t dbuf,
+                                      uint32_t tload) {
   if constexpr (I < 16) {
     if constexpr (I + kPre8 < 16) fr[(I + kPre8) % (kPre8 + 1)] = op8<I + kPre8>(sK, sV, l32, h);
     const i32x8 a = fr[I % (kPre8 + 1)];
@@ -253,12 +288,9 @@ __device__ __forceinline__ void step8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f32x
                             0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
         lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, 0, 0, 0);
       }
-      if constexpr ((I & 1) == 0) {
-        ld.template store_one<((I - 8) >> 1)>(sks, svs, tid);
-        ld.template load_one<((I - 8) >> 1)>(rk, rv, tload, np, tid);
-      }
     }
-    step8<I + 1, NT>(sacc, oacc, lacc, qf, p8, sK, sV, l32, h, fr, ld, sks, svs, rk, rv, tload, np, tid);
+    if constexpr ((I & 1) == 1 && (I >> 1) < TileDma8<NT / 64>::PER) dma.template issue<(I >> 1)>(dbuf, tload);
+    step8<I + 1, NT>(sacc, oacc, lacc, qf, p8, sK, sV, l32, h, fr, dma, dbuf, tload);
   }
 }
 
@@ -267,10 +299,6 @@ __device__ __forceinline__ void step8_schedule() {
   if constexpr (I < 16) {
     if constexpr (I + kPre8 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
     __builtin_amdgcn_sched_group_barrier(0x008, ((I >= 8) && ((I - 8) & 3) == 0) ? 2 : 1, 0);
-    if constexpr (I >= 8 && (I & 1) == 0) {
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS store
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
-    }
     step8_schedule<I + 1>();
   }
 }
@@ -353,7 +381,7 @@ __device__ __forceinline__ void softmax8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-  mx = fmaxf(mx, swap_halves(mx));
+  mx = max_halves(mx);
   const float mnew = fmaxf(m_run, mx * f);
   const float alpha = fast_exp2(m_run - mnew);
   const float moff = mnew - p_off;
@@ -399,8 +427,7 @@ __device__ __forceinline__ void softmax8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f
 template <int NW, bool OUT_F32>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb) {
   constexpr int BM = NW * 32, NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint8_t smK[NB8][BN8 * RS8];
-  __shared__ __attribute__((aligned(16))) uint8_t smV[NB8][D * RS8];
+  __shared__ __attribute__((aligned(16))) uint8_t smT[NB8][kTileBuf8];
   __shared__ uint32_t qmax_lds[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -423,10 +450,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
 
   const uint8_t* k8 = a.k8 + (int64_t)bh * np * D;
   const uint8_t* v8 = a.v8t + (int64_t)bh * D * np;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k8, (uint32_t)(np * D));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v8, (uint32_t)(np * D));
-  const float* skp = a.sk + (int64_t)bh * nb;
-  const float* svp = a.sv + (int64_t)bh * nb;
+  TileDma8<NW> dma;
+  dma.init(__builtin_amdgcn_readfirstlane(wave), lane, k8, v8, np);
+  constexpr int PER = TileDma8<NW>::PER;
+  // The K and V scales are read through the scalar cache (constant address
+  // space; the quantisation pass wrote them before this kernel started): a
+  // vector load here would make the compiler wait for every outstanding
+  // vector memory operation, the in-flight tile staging included.
+  typedef const __attribute__((address_space(4))) float* cfloat_ptr;
+  const cfloat_ptr skp = (cfloat_ptr)(a.sk + (int64_t)bh * nb);
+  const cfloat_ptr svp = (cfloat_ptr)(a.sv + (int64_t)bh * nb);
 
   // Q is quantised here, in the prologue, rather than by the quantisation
   // pass: the work-group's 256 rows are exactly two 128-token scale blocks
@@ -451,16 +484,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
   float m_run = -INFINITY;
   VUnit unit = {svp[t0], svp[t0]};
 
-  // ---- prologue: tiles t0 and t0+1 into LDS, t0+2 into registers ----
-  Loader8<NT> ld;
-  ld.load(rk, rv, t0, np, tid);
+  // ---- prologue: tiles t0 .. t0+2 into LDS buffers 0 .. 2 (past the last
+  // tile the load repeats it into a buffer nobody reads) ----
+  dma.issue_all(lds_addr8(smT[0]), (uint32_t)t0);
   u32x4 qx[2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) qx[s][c4] = buf_load_b128(rq, qoff + (64 * s + 32 * h + 8 * c4) * 2);
-  ld.store(smK[0], smV[0], tid);
-  ld.load(rk, rv, min(t0 + 1, t1 - 1), np, tid);
+  dma.issue_all(lds_addr8(smT[1]), (uint32_t)min(t0 + 1, t1 - 1));
+  dma.issue_all(lds_addr8(smT[2]), (uint32_t)min(t0 + 2, t1 - 1));
   uint32_t qabs = 0;   // max of |x| over this lane's elements, as bf16 bits (ordered like the values)
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -473,8 +506,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
       }
   qabs = wave_max_u32(qabs);
   if (lane == 0) qmax_lds[wave] = qabs;
-  ld.store(smK[1], smV[1], tid);
-  ld.load(rk, rv, min(t0 + 2, t1 - 1), np, tid);
+  dma8_wait_all();
   __syncthreads();
 
   // The Q scale block of this wave: absmax over its four waves, then the
@@ -506,7 +538,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
 
   f32x16 sacc[4];
   uint32_t p8[2][8];
-  qk8_tile(sacc, smK[0], qf, l32, h);
+  qk8_tile(sacc, smT[0], qf, l32, h);
   softmax8(sacc, oacc, lacc, p8, m_run, unit, fq * skp[t0], svp[t0], a.p_off, t0 * BN8, N, h);
 
   // Ping-pong, as in the bf16 dense kernel: waves 4-7 run half a step behind
@@ -514,10 +546,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
   // loop), so on every SIMD one wave's MFMAs overlap the other's softmax.
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
   if (grp == 1) __syncthreads();
-  int bc = 0;   // LDS buffer of tile t; tile t+1 is in bc+1, tile t+2 goes to bc+2 (mod 3)
+  int bc = 0;   // LDS buffer of tile t; tile t+1 is in bc+1, tile t+3 goes to bc+3 (mod 4)
+  float sk_next = skp[min(t0 + 1, t1 - 1)], sv_next = svp[min(t0 + 1, t1 - 1)];   // scales of tile t+1
   for (int t = t0; t + 1 < t1; ++t) {
-    const int bn = (bc + 1 == NB8) ? 0 : bc + 1;
-    const int bn2 = (bn + 1 == NB8) ? 0 : bn + 1;
+    const int bn = (bc + 1) & (NB8 - 1);
+    const int b3 = (bc + 3) & (NB8 - 1);
     // Past the last tile the staged buffer is free and never read, and the
     // load repeats the last tile.
     const int tload = min(t + 3, t1 - 1);
@@ -526,18 +559,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
     i32x8 fr[kPre8 + 1];
-    prefetch8<0>(fr, smK[bn], smV[bc], l32, h);
-    step8<0, NT>(sacc, oacc, lacc, qf, p8, smK[bn], smV[bc], l32, h, fr, ld, smK[bn2], smV[bn2], rk, rv, tload,
-                 np, tid);
+    prefetch8<0>(fr, smT[bn], smT[bc] + kRegion8, l32, h);
+    step8<0, NT>(sacc, oacc, lacc, qf, p8, smT[bn], smT[bc] + kRegion8, l32, h, fr, dma, lds_addr8(smT[b3]),
+                 (uint32_t)tload);
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre8, 0);
     step8_schedule<0>();
-    __syncthreads();
-    softmax8(sacc, oacc, lacc, p8, m_run, unit, fq * skp[t + 1], svp[t + 1], a.p_off, (t + 1) * BN8, N, h);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);   // the whole MFMA stream before the barrier
+    dma8_barrier<PER>();
+    // The scales of the tile after next, read at the start of the softmax,
+    // which makes no LDS access: a scalar load shares its wait counter with
+    // the LDS operand reads, so one still in flight during the MFMA stream
+    // would hold up its first read.  The empty asm keeps the loads here.
+    const int t2 = min(t + 2, t1 - 1);
+    const float sk_nn = skp[t2], sv_nn = svp[t2];
+    asm volatile("" ::: "memory");
+    softmax8(sacc, oacc, lacc, p8, m_run, unit, fq * sk_next, sv_next, a.p_off, (t + 1) * BN8, N, h);
+    sk_next = sk_nn;
+    sv_next = sv_nn;
+    plain_barrier8();
     bc = bn;
   }
+  dma8_wait_all();
   if (grp == 0) __syncthreads();
-  pv8_tile(oacc, lacc, p8, smV[bc], l32, h);
+  pv8_tile(oacc, lacc, p8, smT[bc] + kRegion8, l32, h);
 
   // ---- epilogue: O = A * sV_last / l ----
   const int64_t ob = b * a.os[0] + hd * a.os[1];
