@@ -31,11 +31,11 @@
 // one (batch, head) per work-group, two waves per SIMD.  Each wave's rows are
 // three 16-row blocks on the 16x16x32 bf16 MFMA, so every K fragment and V
 // operand read from LDS feeds three MFMAs (a third less LDS traffic per flop
-// than 32-row waves).  K and V stream through LDS in 32-key tiles in three
-// rotating buffers.  Step t issues the QK^T MFMAs of tile t+1 and the PV
-// MFMAs of tile t as one stream with their LDS operands read ahead; the LDS
-// stores of tile t+2 and the global loads of tile t+3 ride on the PV MFMAs;
-// then the softmax of tile t+1.  Waves 4-7 run half a step behind waves 0-3
+// than 32-row waves).  K and V stream through LDS in 32-key tiles in four
+// rotating buffers, loaded straight from global memory into LDS.  Step t
+// issues the QK^T MFMAs of tile t+1 and the PV MFMAs of tile t as one stream
+// with their LDS operands read ahead, and the loads of tile t+3 beside its
+// first MFMAs; then the softmax of tile t+1.  Waves 4-7 run half a step behind waves 0-3
 // (two barriers per step), so on each SIMD one wave's MFMA stream runs while
 // the other wave does its softmax.
 //
@@ -540,9 +540,9 @@ __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
 // blocks each, on the 16x16x32 MFMA), two work-groups per CU.  The key
 // tiles are the 32-key tiles of the row's kept 128-key blocks, in order
 // (masked blocks are never loaded); they flow through the dense kernel's
-// pipeline: three LDS buffers, step t = QK^T of tile t+1 and PV of tile t
-// with tile t+2 stored to LDS and tile t+3 loaded beside the PV MFMAs, a
-// barrier, then the softmax of tile t+1; row sums on the matrix core; the
+// pipeline: four LDS buffers, step t = QK^T of tile t+1 and PV of tile t
+// with tile t+3 loaded into LDS beside them, a barrier, then the softmax of
+// tile t+1; row sums on the matrix core; the
 // lazy reference with the end-of-row 2^80 check and an exact second pass.
 
 // Key offsets of the successive 32-key tiles of the kept 128-key blocks of

@@ -13,7 +13,7 @@
 //   into LDS without any shuffle.
 //
 // Attention (work-group = 8 waves x 32 query rows, two waves per SIMD; key
-// tiles of 128 = one scale block, in three rotating LDS buffers; the QK^T
+// tiles of 128 = one scale block, in four rotating LDS buffers; the QK^T
 // MFMAs of tile t+1 and the PV MFMAs of tile t form one stream with their
 // LDS operands read ahead, then the softmax of tile t+1; waves 4-7 run half
 // a step behind waves 0-3, two barriers per step),
@@ -420,10 +420,10 @@ __device__ __forceinline__ void softmax8(f32x16 (&sacc)[4], f32x16 (&oacc)[4], f
 
 // Work-group: NW waves x 32 query rows.  Step t issues the QK^T MFMAs of
 // tile t+1 and the PV MFMAs of tile t as one stream, their A operands read
-// from LDS kPre8 MFMAs ahead, with tile t+2 stored to LDS and tile t+3
-// loaded into registers beside the PV half; a barrier; then the softmax of
-// tile t+1 and a second barrier, with waves 4-7 half a step behind waves
-// 0-3.  Tiles rotate through NB8 LDS buffers.
+// from LDS kPre8 MFMAs ahead, with tile t+3 loaded straight into LDS beside
+// them; a barrier; then the softmax of tile t+1 and a second barrier, with
+// waves 4-7 half a step behind waves 0-3.  Tiles rotate through NB8 LDS
+// buffers.
 template <int NW, bool OUT_F32>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(Fp8Args a, int nqb) {
   constexpr int BM = NW * 32, NT = NW * 64;
