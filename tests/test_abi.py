@@ -73,6 +73,9 @@ def _fwd(s, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None):
     (lambda s: s.v_stride.__setitem__(1, -8), INVALID),
     (lambda s: s.o_stride.__setitem__(0, 12), INVALID),
     (lambda s: (setattr(s, "seqlen", 1 << 22), s.q_stride.__setitem__(2, 1024)), UNSUPPORTED),
+    # a row stride above 2^22 elements (the staged key tiles' 32-bit offsets
+    # past the last row could wrap), even where the slice itself is small
+    (lambda s: (setattr(s, "seqlen", 2), s.k_stride.__setitem__(2, (1 << 22) + 8)), UNSUPPORTED),
 ])
 def test_fwd_rejects_bad_shapes(mutate, status):
     s = _shape()
