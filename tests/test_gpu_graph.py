@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import joint_attention_non_amd as dit
-from workloads import make_block_mask, make_qkv
+from workloads import make_block_mask, make_local_qkv, make_qkv
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -83,3 +83,24 @@ def test_graph_blocksparse():
     call()
     torch.cuda.synchronize()
     _replays_match(call, (o, lse), (o.clone(), lse.clone()))
+
+
+def test_graph_select_then_blocksparse():
+    """The selection and the block-sparse attention on its mask, captured
+    together in one graph (three kernels: pooling, selection, attention)."""
+    N = 3000
+    _say(f"case: graph capture dit_attn_select_blocks + blocksparse B1 H3 N{N}")
+    q, k, v = (t.to(DEV) for t in make_local_qkv(1, 3, N, 256, seed=113))
+    nb = (N + 127) // 128
+    mask = torch.empty((1, 3, nb, nb), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(dit.select_blocks_workspace_bytes(q), dtype=torch.uint8, device=DEV)
+    o = torch.empty((1, 3, N, 128), dtype=torch.float32, device=DEV)
+
+    def call():
+        dit.select_blocks(q, k, 1.0, 256, out=mask, workspace=ws)
+        dit.attn_fwd_blocksparse(q, k, v, mask, out=o, out_fp32=True)
+
+    call()
+    torch.cuda.synchronize()
+    assert 0 < int(mask.sum()) < mask.numel()
+    _replays_match(call, (mask, o), (mask.clone(), o.clone()))
