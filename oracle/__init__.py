@@ -26,6 +26,12 @@ Functions and what pins them (tests/test_oracle.py):
   must match a restatement with torch's e4m3 cast (and differ from the
   final-max variant), and its error against ``attn`` on the unquantised inputs
   must sit in the band the e4m3 step implies.
+* ``attn_fp8_recipe(..., nsplit=S)`` -- the recipe with each row's key
+  blocks cut into S ranges, each from a fresh running max, merged exactly;
+  pinned by S = 1 being the recipe bit for bit, by S = 3 without P
+  quantisation equalling ``attn`` on the dequantised inputs, by one range
+  per key block matching a numpy / torch-codec restatement, and by S = 3
+  with P quantisation differing from the unsplit recipe (negative control).
 * ``select_blocks``     -- the block-mask selection rule; pinned against
   torch's block pooling and scipy's softmax, the softmax's shift invariance,
   key-block permutation, identical key blocks (every share exactly 1/nb),
@@ -74,6 +80,9 @@ def _load():
         lib.oracle_attn_fp8_recipe.argtypes = [i64, i64, i64, i64, u8p, u8p, u8p, fp, fp, fp,
                                                ctypes.c_double, ctypes.c_int, dp, i64, dp, dp]
         lib.oracle_attn_fp8_recipe.restype = ctypes.c_int
+        lib.oracle_attn_fp8_recipe_split.argtypes = [i64, i64, i64, i64, u8p, u8p, u8p, fp, fp, fp,
+                                                     ctypes.c_double, ctypes.c_int, i64, dp, i64, dp, dp]
+        lib.oracle_attn_fp8_recipe_split.restype = ctypes.c_int
         lib.oracle_select_blocks.argtypes = [i64, i64, i64, i64, dp, dp, ctypes.c_double,
                                              ctypes.c_double, i64, u8p, dp]
         lib.oracle_select_blocks.restype = None
@@ -173,8 +182,10 @@ def e4m3_decode_array(codes: np.ndarray) -> np.ndarray:
 
 
 def attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale: float, quantize_p: bool = True,
-                    block: int = 128, rows=None):
-    """The fp8 recipe on oracle-quantised codes; returns (o, lse) like ``attn``."""
+                    block: int = 128, rows=None, nsplit: int = 1):
+    """The fp8 recipe on oracle-quantised codes; returns (o, lse) like ``attn``.
+    nsplit > 1: each row's key blocks cut into nsplit consecutive ranges, each
+    run from a fresh running max, merged exactly (see attn_oracle.c)."""
     q8, k8, v8 = (np.ascontiguousarray(a, dtype=np.uint8) for a in (q8, k8, v8))
     sq, sk, sv = (np.ascontiguousarray(a, dtype=np.float32) for a in (sq, sk, sv))
     if q8.ndim != 4 or k8.shape != q8.shape or v8.shape != q8.shape:
@@ -194,12 +205,12 @@ def attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale: float, quantize_p: bool = Tru
         nrows = BH * N
     o = np.empty((nrows, D), dtype=np.float64)
     lse = np.empty((nrows,), dtype=np.float64)
-    rc = _load().oracle_attn_fp8_recipe(BH, N, D, block, _ptr(q8), _ptr(k8), _ptr(v8),
-                                        _ptr(sq), _ptr(sk), _ptr(sv), float(scale),
-                                        1 if quantize_p else 0, _ptr(r), nrows,
-                                        _ptr(o), _ptr(lse))
+    rc = _load().oracle_attn_fp8_recipe_split(BH, N, D, block, _ptr(q8), _ptr(k8), _ptr(v8),
+                                              _ptr(sq), _ptr(sk), _ptr(sv), float(scale),
+                                              1 if quantize_p else 0, int(nsplit), _ptr(r), nrows,
+                                              _ptr(o), _ptr(lse))
     if rc != 0:
-        raise ValueError("oracle_attn_fp8_recipe rejected its arguments")
+        raise ValueError("oracle_attn_fp8_recipe_split rejected its arguments")
     if rows is None:
         return o.reshape(B, H, N, D), lse.reshape(B, H, N)
     return o, lse

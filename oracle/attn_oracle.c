@@ -227,27 +227,89 @@ void oracle_fp8_quantize(int64_t BH, int64_t N, int64_t D, int64_t block,
  *   o_d   = acc_d / l,   lse = m_last + ln l
  *
  * 448 * w_j is formed in fp32 (the precision the device uses for that
- * rounding decision) before encoding; everything else is fp64. */
-int oracle_attn_fp8_recipe(int64_t BH, int64_t N, int64_t D, int64_t block,
-                           const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
-                           const float* sq, const float* sk, const float* sv,
-                           double scale, int quantize_p,
-                           const int64_t* rows, int64_t nrows,
-                           double* o, double* lse)
+ * rounding decision) before encoding; everything else is fp64.
+ *
+ * recipe_range runs these steps for one row over key blocks [kb0, kb1),
+ * starting from m = -inf, l = 0, acc = 0, and leaves acc, m and l. */
+typedef struct {
+    int64_t N, D, block, nb;
+    const uint8_t *k8, *v8;
+    const float *sq, *sk, *sv;
+    double scale;
+    int quantize_p;
+    const double* dec;
+} recipe_in;
+
+static void recipe_range(const recipe_in* in, int64_t bh, int64_t qb, const double* qd, int64_t kb0,
+                         int64_t kb1, double* t, double* acc, double* m_out, double* l_out)
+{
+    const int64_t N = in->N, D = in->D, block = in->block, nb = in->nb;
+    const double* dec = in->dec;
+    double m = -INFINITY, l = 0.0;
+    for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+    for (int64_t kb = kb0; kb < kb1; ++kb) {
+        const int64_t j0 = kb * block, j1 = (j0 + block < N) ? j0 + block : N;
+        const double f = in->scale * (double)in->sq[bh * nb + qb] * (double)in->sk[bh * nb + kb];
+        double mt = -INFINITY;
+        for (int64_t j = j0; j < j1; ++j) {
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += qd[d] * dec[in->k8[(bh * N + j) * D + d]];
+            t[j - j0] = f * dot;
+            if (t[j - j0] > mt) mt = t[j - j0];
+        }
+        const double mnew = (mt > m) ? mt : m;
+        const double alpha = (m == -INFINITY) ? 0.0 : exp(m - mnew);
+        l *= alpha;
+        for (int64_t d = 0; d < D; ++d) acc[d] *= alpha;
+        const double svk = (double)in->sv[bh * nb + kb];
+        for (int64_t j = j0; j < j1; ++j) {
+            const double w = exp(t[j - j0] - mnew);
+            const float y = (float)w * 448.0f;
+            const double p = in->quantize_p ? dec[oracle_e4m3_encode((double)y)] : 448.0 * w;
+            l += p / 448.0;
+            const double c = p / 448.0 * svk;
+            for (int64_t d = 0; d < D; ++d) acc[d] += c * dec[in->v8[(bh * N + j) * D + d]];
+        }
+        m = mnew;
+    }
+    *m_out = m;
+    *l_out = l;
+}
+
+/* The recipe with each row's key blocks cut into nsplit consecutive ranges
+ * (range p = blocks p*nb/nsplit .. (p+1)*nb/nsplit - 1, integer division),
+ * each run by recipe_range from its own fresh running max, and the ranges
+ * merged exactly:
+ *   M = max_p m_p,   o = sum_p exp(m_p - M) acc_p / sum_p exp(m_p - M) l_p,
+ *   lse = M + ln sum_p exp(m_p - M) l_p.
+ * nsplit = 1 is the recipe above (M = m, every factor exp(0) = 1).  This is
+ * what a query block computes when its key range is split over several
+ * workers: each range rounds its P against its own running max.
+ * 1 <= nsplit <= nb, else -1. */
+int oracle_attn_fp8_recipe_split(int64_t BH, int64_t N, int64_t D, int64_t block,
+                                 const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                                 const float* sq, const float* sk, const float* sv,
+                                 double scale, int quantize_p, int64_t nsplit,
+                                 const int64_t* rows, int64_t nrows,
+                                 double* o, double* lse)
 {
     if (BH <= 0 || N <= 0 || D <= 0 || block <= 0) return -1;
-    if (!rows) nrows = BH * N;
     const int64_t nb = (N + block - 1) / block;
+    if (nsplit < 1 || nsplit > nb) return -1;
+    if (!rows) nrows = BH * N;
     double dec[256];
     for (int c = 0; c < 256; ++c) dec[c] = oracle_e4m3_decode((uint8_t)c);
+    const recipe_in in = {N, D, block, nb, k8, v8, sq, sk, sv, scale, quantize_p, dec};
     int bad = 0;
 
 #pragma omp parallel
     {
-        double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)(D * nsplit));
+        double* mp = (double*)malloc(sizeof(double) * (size_t)nsplit);
+        double* lp = (double*)malloc(sizeof(double) * (size_t)nsplit);
         double* t = (double*)malloc(sizeof(double) * (size_t)block);
         double* qd = (double*)malloc(sizeof(double) * (size_t)D);
-        if (!acc || !t || !qd) {
+        if (!acc || !mp || !lp || !t || !qd) {
 #pragma omp atomic write
             bad = 1;
         } else {
@@ -261,42 +323,41 @@ int oracle_attn_fp8_recipe(int64_t BH, int64_t N, int64_t D, int64_t block,
                 }
                 const int64_t bh = row / N, i = row % N, qb = i / block;
                 for (int64_t d = 0; d < D; ++d) qd[d] = dec[q8[(bh * N + i) * D + d]];
-                double m = -INFINITY, l = 0.0;
-                for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
-                for (int64_t kb = 0; kb < nb; ++kb) {
-                    const int64_t j0 = kb * block, j1 = (j0 + block < N) ? j0 + block : N;
-                    const double f = scale * (double)sq[bh * nb + qb] * (double)sk[bh * nb + kb];
-                    double mt = -INFINITY;
-                    for (int64_t j = j0; j < j1; ++j) {
-                        double dot = 0.0;
-                        for (int64_t d = 0; d < D; ++d) dot += qd[d] * dec[k8[(bh * N + j) * D + d]];
-                        t[j - j0] = f * dot;
-                        if (t[j - j0] > mt) mt = t[j - j0];
-                    }
-                    const double mnew = (mt > m) ? mt : m;
-                    const double alpha = (m == -INFINITY) ? 0.0 : exp(m - mnew);
-                    l *= alpha;
-                    for (int64_t d = 0; d < D; ++d) acc[d] *= alpha;
-                    const double svk = (double)sv[bh * nb + kb];
-                    for (int64_t j = j0; j < j1; ++j) {
-                        const double w = exp(t[j - j0] - mnew);
-                        const float y = (float)w * 448.0f;
-                        const double p = quantize_p ? dec[oracle_e4m3_encode((double)y)] : 448.0 * w;
-                        l += p / 448.0;
-                        const double c = p / 448.0 * svk;
-                        for (int64_t d = 0; d < D; ++d) acc[d] += c * dec[v8[(bh * N + j) * D + d]];
-                    }
-                    m = mnew;
+                double M = -INFINITY;
+                for (int64_t p = 0; p < nsplit; ++p) {
+                    recipe_range(&in, bh, qb, qd, p * nb / nsplit, (p + 1) * nb / nsplit, t, acc + p * D,
+                                 &mp[p], &lp[p]);
+                    if (mp[p] > M) M = mp[p];
                 }
-                for (int64_t d = 0; d < D; ++d) o[r * D + d] = acc[d] / l;
-                if (lse) lse[r] = m + log(l);
+                double l = 0.0;
+                for (int64_t d = 0; d < D; ++d) o[r * D + d] = 0.0;
+                for (int64_t p = 0; p < nsplit; ++p) {
+                    const double wgt = exp(mp[p] - M);
+                    l += wgt * lp[p];
+                    for (int64_t d = 0; d < D; ++d) o[r * D + d] += wgt * acc[p * D + d];
+                }
+                for (int64_t d = 0; d < D; ++d) o[r * D + d] /= l;
+                if (lse) lse[r] = M + log(l);
             }
         }
         free(acc);
+        free(mp);
+        free(lp);
         free(t);
         free(qd);
     }
     return bad ? -1 : 0;
+}
+
+int oracle_attn_fp8_recipe(int64_t BH, int64_t N, int64_t D, int64_t block,
+                           const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                           const float* sq, const float* sk, const float* sv,
+                           double scale, int quantize_p,
+                           const int64_t* rows, int64_t nrows,
+                           double* o, double* lse)
+{
+    return oracle_attn_fp8_recipe_split(BH, N, D, block, q8, k8, v8, sq, sk, sv, scale, quantize_p, 1, rows,
+                                        nrows, o, lse);
 }
 
 /* Block-mask selection in the manner of Sol-Attention (block-sparse attention

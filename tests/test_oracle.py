@@ -449,6 +449,58 @@ def test_fp8_recipe_running_max_across_key_blocks(N, gaps):
     assert np.max(np.abs(o[0] - wrong)) >= 1e-4
 
 
+def _recipe_one_range_per_block_numpy(q8, k8, v8, sq, sk, sv, scale, i, block=128):
+    """Row i of (0, 0) with every key block its own range, restated with numpy
+    and torch's e4m3 codec: each block's P8 rounded against that block's own
+    max, then the blocks merged with exp(m_b - M)."""
+    N = q8.shape[2]
+    nb = (N + block - 1) // block
+    qd = _torch_dec(q8[0, 0, i])
+    kd, vd = _torch_dec(k8[0, 0]), _torch_dec(v8[0, 0])
+    qb = i // block
+    parts = []
+    for kb in range(nb):
+        tb = scale * float(sq[0, 0, qb]) * float(sk[0, 0, kb]) * (kd[kb * block:(kb + 1) * block] @ qd)
+        mb = tb.max()
+        p = _torch_dec(_torch_e4m3(np.exp(tb - mb).astype(np.float32) * np.float32(448.0))) / 448.0
+        parts.append((mb, p.sum(), float(sv[0, 0, kb]) * (p @ vd[kb * block:(kb + 1) * block])))
+    M = max(m for m, _, _ in parts)
+    l = sum(math.exp(m - M) * lp for m, lp, _ in parts)
+    acc = sum(math.exp(m - M) * a for m, _, a in parts)
+    return acc / l, M + math.log(l)
+
+
+def test_fp8_recipe_split_into_key_ranges():
+    """The recipe with each row's key blocks cut into ranges, each from a
+    fresh running max, merged exactly: one range is the recipe; without P
+    quantisation any cut gives the textbook attention on the dequantised
+    inputs (the merge is exact); one range per block matches an independent
+    restatement; with P quantisation a cut changes the result (each range
+    rounds P against its own max) by about the e4m3 step."""
+    N = 700                                   # 6 key blocks, the last ragged
+    _, (q8, k8, v8, sq, sk, sv) = _quantized_inputs(N, 21, H=2)
+    scale = 1.0 / math.sqrt(128)
+    o1, l1 = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale)
+    o1s, l1s = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale, nsplit=1)
+    assert np.array_equal(o1, o1s) and np.array_equal(l1, l1s)
+    o3, l3 = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale, quantize_p=False, nsplit=3)
+    qd, kd, vd = _dequant(q8, sq), _dequant(k8, sk), _dequant(v8, sv)
+    ref, ref_lse = oracle.attn(qd, kd, vd, scale)
+    assert np.max(np.abs(o3 - ref)) <= 1e-12
+    assert np.max(np.abs(l3 - ref_lse)) <= 1e-12
+    o6, l6 = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale, nsplit=6)
+    for i in (0, 5, 300, 699):
+        want, want_lse = _recipe_one_range_per_block_numpy(q8, k8, v8, sq, sk, sv, scale, i)
+        assert np.max(np.abs(o6[0, 0, i] - want)) <= 1e-12
+        assert abs(l6[0, 0, i] - want_lse) <= 1e-12
+    o3q, _ = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale, nsplit=3)
+    diff = o3q - o1
+    assert np.max(np.abs(diff)) >= 1e-5
+    assert np.linalg.norm(diff) / np.linalg.norm(o1) <= 0.05
+    with pytest.raises(ValueError):
+        oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, scale, nsplit=7)   # more ranges than blocks
+
+
 def test_fp8_quantize_tiny_block_is_a_zero_block():
     """448 / absmax overflows fp32 for absmax below 448 / FLT_MAX (~1.3e-36):
     such a block is stored like an all-zero one (scale 1, codes +0), also when
