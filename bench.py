@@ -160,10 +160,22 @@ def _graph_us_per_launch(call, n, torch):
     return e0.elapsed_time(e1) * 1e3 / (reps * n)
 
 
-def _fp8_accuracy(wf, rows, got):
+def _fp8_split_plan(B, H, N, cus):
+    """(first split block, ranges) of the fp8 attention grid on `cus` compute
+    units: 256-row query blocks, the last partial round cut into key ranges
+    of 128-key tiles (none when the grid is whole rounds or smaller than one)."""
+    units = B * H * ((N + 255) // 256)
+    full, r = divmod(units, cus)
+    split = min(cus // r, (N + 127) // 128) if (full >= 1 and r > 0) else 1
+    return (units - r, split) if split >= 2 else (units, 1)
+
+
+def _fp8_accuracy(wf, rows, got, cus):
     """Part of the oracle leg: the fp8 output on `rows` (first, last and one
     random row of every 256-row work-group) against the oracle's exact
-    attention on the unquantised inputs and against its fp8 recipe."""
+    attention on the unquantised inputs, against its fp8 recipe, and against
+    the recipe as the library applies it (rows of the split last round: the
+    recipe cut into the same key ranges, merged exactly)."""
     import numpy as np
     import oracle
     from workloads import make_workload_inputs
@@ -173,6 +185,14 @@ def _fp8_accuracy(wf, rows, got):
     k8, sk = oracle.fp8_quantize(k)
     v8, sv = oracle.fp8_quantize(v)
     rec, _ = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, wf.scale, rows=rows)
+    first, split = _fp8_split_plan(wf.batch, wf.heads, wf.seqlen, cus)
+    nqb = (wf.seqlen + 255) // 256
+    r = rows.numpy()
+    in_split = (r // wf.seqlen) * nqb + (r % wf.seqlen) // 256 >= first
+    rec_lib = rec.copy()
+    if in_split.any():
+        rec_lib[in_split], _ = oracle.attn_fp8_recipe(q8, k8, v8, sq, sk, sv, wf.scale, rows=rows[in_split],
+                                                      nsplit=split)
     a = got.double().numpy().ravel()
 
     def cmp(b):
@@ -183,6 +203,7 @@ def _fp8_accuracy(wf, rows, got):
     rr = rec.ravel()
     b = ref.ravel()
     return {"rows": int(rows.numel()), "vs_exact": e_ref, "vs_recipe": e_rec,
+            "vs_recipe_as_applied": dict(cmp(rec_lib), split_rows=int(in_split.sum()), ranges=split),
             "recipe_vs_exact_rel_l2": round(float(np.linalg.norm(rr - b) / np.linalg.norm(b)), 5),
             "gate": {"cos_min": 0.99, "rel_l2_max": 0.05,
                      "cos_met": e_ref["cos"] >= 0.99, "rel_l2_met": e_ref["rel_l2"] <= 0.05}}
@@ -399,7 +420,8 @@ def main():
         log(f"[bench] cpu: {cpu}")
         if fp8_inputs is not None:
             log("[bench] fp8 accuracy against the oracle (rows of every work-group)")
-            legs["img2048_fp8"]["accuracy"] = _fp8_accuracy(*fp8_inputs)
+            legs["img2048_fp8"]["accuracy"] = _fp8_accuracy(
+                *fp8_inputs, torch.cuda.get_device_properties(0).multi_processor_count)
             log(f"[bench] fp8 accuracy: {legs['img2048_fp8']['accuracy']}")
 
     line = {
