@@ -91,10 +91,17 @@ def _launch_stats(fn, steps, torch, flush_mib=512):
 
 
 def _source_sha(*names):
+    """sha256[:16] of the kernel sources with comments and blank space
+    removed, so that an edit to a comment keeps the counters' record valid
+    while any change to the code voids it."""
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "joint_attention_non_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "joint_attention_non_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

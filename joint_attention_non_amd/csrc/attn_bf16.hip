@@ -61,7 +61,13 @@ namespace dit {
 namespace {
 
 constexpr int D = kHeadDim;
-constexpr int KS = D + 8;     // K tile row stride in bf16 (272 B: conflict-free b128 reads)
+// K tile row stride in bf16: 272 B.  The QK^T operand reads (lane (g, l16)
+// takes 16 bytes of row l16 at chunk 4 ds + g) cost 4 LDS bank-conflict
+// cycles each at this stride (SQ_LDS_BANK_CONFLICT), none at 288 or 352 B or
+// with 256-byte rows whose 16-byte chunks are XOR-ed with the row; but with
+// those layouts the dense kernel measured 6-10 % slower (its matrix cores
+// idled more), so the padded 272-byte rows stay.
+constexpr int KS = D + 8;
 // When the reference max is recomputed (first tile, or a redo after a huge
 // jump), it only moves if some row of the wave grew by more than 2^kLazy.
 constexpr float kLazy = 8.f;
