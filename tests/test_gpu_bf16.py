@@ -269,3 +269,28 @@ def test_long_sequence_sampled_parity():
     e = errors(o32.reshape(-1, 128)[rows.to(DEV)].cpu(), ref)
     _say(f"fp32-out {e}")
     assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
+
+
+def test_largest_row_stride():
+    """Rows 2^22 elements apart, the largest stride the boundary accepts: the
+    key tiles staged past the last row (up to 127 rows beyond N) sit at
+    32-bit byte offsets near 2^30 that must read as zeros.  Dense (with and
+    without the tail split) and block-sparse against the oracle."""
+    N, S = 200, 1 << 22           # one (b, h) slice spans 1.7 GB, below the 2 GiB limit
+    _say(f"case: row stride {S} elements, N={N}")
+    base = torch.zeros((3, N, S), dtype=torch.bfloat16, device=DEV)   # 5 GB
+    q, k, v = make_qkv(1, 1, N, 128, seed=131)
+    for i, t in enumerate((q, k, v)):
+        base[i, :, :128] = t[0, 0].to(DEV)
+    qd, kd, vd = (base[i, :, :128].unsqueeze(0).unsqueeze(0) for i in range(3))
+    assert qd.stride(2) == S
+    ref, _ = oracle.attn(q, k, v, 1.0 / math.sqrt(128))
+    outs = [dit.attn_fwd(qd, kd, vd, out_fp32=True),
+            dit.attn_fwd(qd, kd, vd, out_fp32=True, workspace=dit.fwd_workspace(qd))]
+    mask = torch.ones((2, 2), dtype=torch.uint8, device=DEV)
+    outs.append(dit.attn_fwd_blocksparse(qd, kd, vd, mask, out_fp32=True))
+    torch.cuda.synchronize()
+    for o in outs:
+        e = errors(o, ref)
+        assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
+    del base
