@@ -13,8 +13,9 @@
  * with no causal mask.  The pages select among a "VANILLA" BF16 attention,
  * quantised FP8 attention, and block-sparse attention backends (scopeai.cc
  * page, section "各项优化的效果与质量代价"; bpdata.com page, section "Mi
- * szerepel az optimalizálásban"); the three calls below are this library's
- * versions of those three.
+ * szerepel az optimalizálásban"); the three attention calls below are this
+ * library's versions of those three, and dit_attn_select_blocks chooses the
+ * block mask for the block-sparse one.
  *
  * Conventions shared by every call.
  *  - Tensors.  Q, K, V and O are [B, H, N, D] with element strides given per
@@ -25,7 +26,9 @@
  *    exp(scale * <q_i, k_j>) over the keys the row attends to.  Pass NULL to
  *    skip it.  A row that attends to no key gets O = 0 and lse = -inf.
  *  - Pointers are device pointers.  Q, K, V, O must be 16-byte aligned; every
- *    (b, h, n) stride of Q, K, V and O must be a multiple of 8 elements.
+ *    (b, h, n) stride of Q, K, V and O must be a multiple of 8 elements, a
+ *    row stride at most 2^22 elements, and one (b, h) slice must span less
+ *    than 2 GiB (DIT_ATTN_ERR_UNSUPPORTED otherwise).
  *  - Ownership.  The caller owns every buffer and the stream; the library
  *    never allocates or frees memory.
  *  - Asynchrony.  Calls enqueue work on `stream` (a hipStream_t; NULL is the
@@ -36,8 +39,9 @@
  *    dit_attn_last_error() then gives a per-thread description.
  *  - Determinism.  For a fixed build, device and arguments the output is
  *    bitwise reproducible: reductions use no atomics and a fixed key order.
- *  - Thread safety.  Calls are re-entrant; there is no global mutable state
- *    besides the per-thread error string.
+ *  - Thread safety.  Calls are re-entrant.  Global state: the per-thread
+ *    error string, per-device caches filled once (compute-unit count, the
+ *    address of dit_attn_fwd_noalloc's array) and that array itself.
  */
 #ifndef DIT_ATTN_H
 #define DIT_ATTN_H
@@ -80,7 +84,7 @@ typedef struct dit_attn_shape {
  * softmax in fp32, P rounded to bf16 for the PV product.  Query blocks of
  * 384 rows run one per compute unit; when their count leaves a partial last
  * round, dit_attn_fwd_ws (same result within rounding, caller workspace) is
- * faster: 6.15 against 5.5 ms at B2 H24 N16896 on 256 CUs. */
+ * faster: 4.66 against 4.98 ms at B2 H24 N16896 on 256 CUs. */
 int dit_attn_fwd(const dit_attn_shape* shape,
                  const void* q, const void* k, const void* v,
                  void* o, float* lse, void* stream);
@@ -154,7 +158,9 @@ size_t dit_attn_fwd_fp8_workspace_bytes(const dit_attn_shape* shape);
  * Dynamische Quantisierung") applied to attention: Q, K and V are quantised
  * to OCP e4m3 with one scale per (b, h, 128-token block):
  *     s = absmax / 448,  code = e4m3_rne(clamp(x * (448 / absmax), +-448))
- * (absmax == 0 gives s = 1 and zero codes).  QK^T runs on fp8 MFMA; the
+ * (a block whose 448 / absmax is not a finite fp32 number -- absmax 0, or
+ * below 448 / FLT_MAX -- gets s = 1 and zero codes).  QK^T runs on fp8
+ * MFMA; the
  * online softmax keeps a running max per 128-key block; the unnormalised
  * probabilities w in [0, 1] are quantised as e4m3(448 w) for the fp8 PV
  * product, and the row sum is taken over the same quantised weights (so the
