@@ -553,11 +553,16 @@ __global__ __launch_bounds__(RNT, 2) void attn_dense_kernel(AttnArgs a) {
 
 // Key offsets of the successive 32-key tiles of the kept 128-key blocks of
 // one mask row; the row is scanned 64 entries at a time with a ballot, so
-// every value here is wave-uniform.  -1 when the row is exhausted.
+// every value here is wave-uniform.  -1 when the row is exhausted.  The
+// first 32 chunks' entries are read at init (bit c of `pre`: this lane's
+// entry of chunk c is kept): a mask read inside the key loop would wait for
+// every outstanding load of the wave, the tile staging loads included.
 struct SparseTileQueue {
   const uint8_t* row;
   int nb, N, chunk, blk, sub;
   uint64_t bits;
+  uint32_t pre;
+  static constexpr int kPreChunks = 32;
   __device__ __forceinline__ void init(const uint8_t* r, int nb_, int N_) {
     row = r;
     nb = nb_;
@@ -566,6 +571,18 @@ struct SparseTileQueue {
     blk = -1;
     sub = 0;
     bits = 0;
+    pre = 0;
+    const int lane = (int)(threadIdx.x & 63);
+    // four chunks per round, their loads issued together (index clamped to
+    // the row), one wait per round
+    for (int c0 = 0; c0 < kPreChunks && c0 * 64 < nb; c0 += 4) {
+      uint32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = row[min((c0 + u) * 64 + lane, nb - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        pre |= ((c0 + u) * 64 + lane < nb && v[u] != 0) ? (1u << (c0 + u)) : 0u;
+    }
   }
   __device__ __forceinline__ int next() {
     if (blk >= 0) {
@@ -579,9 +596,13 @@ struct SparseTileQueue {
         blk = -1;
         return -1;
       }
-      const int j = chunk * 64 + (int)(threadIdx.x & 63);
-      const int keep = (j < nb) ? (int)row[j] : 0;
-      bits = __ballot(keep != 0);
+      if (chunk < kPreChunks) {
+        bits = __ballot(((pre >> chunk) & 1u) != 0);
+      } else {
+        const int j = chunk * 64 + (int)(threadIdx.x & 63);
+        const int keep = (j < nb) ? (int)row[j] : 0;
+        bits = __ballot(keep != 0);
+      }
     }
     const int b = __builtin_ctzll(bits);
     bits &= bits - 1;
