@@ -84,7 +84,7 @@ typedef struct dit_attn_shape {
  * softmax in fp32, P rounded to bf16 for the PV product.  Query blocks of
  * 384 rows run one per compute unit; when their count leaves a partial last
  * round, dit_attn_fwd_ws (same result within rounding, caller workspace) is
- * faster: 4.66 against 4.98 ms at B2 H24 N16896 on 256 CUs. */
+ * faster: 4.66-4.76 against 4.98-5.01 ms at B2 H24 N16896 on 256 CUs. */
 int dit_attn_fwd(const dit_attn_shape* shape,
                  const void* q, const void* k, const void* v,
                  void* o, float* lse, void* stream);
