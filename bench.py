@@ -270,7 +270,10 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": "attn_dense_kernel<false>",
-                "flops_per_launch": flops}
+                "flops_per_launch": flops,
+                # achieved HBM rate: the counted bytes over the timed step
+                "traffic_gbs": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),
+                "traffic_frac_of_hbm": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     log(f"[bench] {w.name}: {ms:.3f} ms  {tflops:.1f} TFLOP/s  {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak"
         f"  (without the tail split {ms_plain:.3f} ms)")
     del o, wsb
