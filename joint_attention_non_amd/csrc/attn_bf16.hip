@@ -155,10 +155,12 @@ struct TileDma {
   template <int J>
   __device__ __forceinline__ void issue(uint32_t buf, uint32_t key0) const {
     const uint32_t voff = off[J] + key0 * srow[J];
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    // The LDS address goes in through M0 as an operand, so the compiler
+    // writes M0 itself and knows it was changed.
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "s"(buf + dst[J]), "v"(voff), "s"(rsrc[J])
-                 : "memory", "m0");
+                 : "v"(voff), "s"(rsrc[J]), "{m0}"(buf + dst[J])
+                 : "memory");
   }
   template <int J = 0>
   __device__ __forceinline__ void issue_all(uint32_t buf, uint32_t key0) const {
