@@ -168,3 +168,26 @@ def test_long_sequence_sparse_sampled_parity():
     e = errors(o32.reshape(-1, 128)[rows.to(DEV)].cpu(), ref)
     _say(f"fp32-out {e}")
     assert e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS, e
+
+
+def test_blocksparse_bitwise_determinism():
+    """Repeated calls give the same bits (O and lse): per-head masks of mixed
+    density on a ragged shape, three launches, and the img2048_sparse
+    workload, two launches."""
+    _say("case: block-sparse determinism B1 H4 N3000 and img2048_sparse")
+    N = 3000
+    nb = (N + 127) // 128
+    q, k, v = (t.to(DEV) for t in make_qkv(1, 4, N, 128, seed=97))
+    masks = torch.stack([make_block_mask(N, 64, d, seed=60 + i)
+                         for i, d in enumerate([0.1, 0.3, 0.6, 1.0])]).reshape(1, 4, nb, nb).to(DEV)
+    runs = [dit.attn_fwd_blocksparse(q, k, v, masks, return_lse=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, lse in runs[1:]:
+        assert torch.equal(o.view(torch.int16), runs[0][0].view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), runs[0][1].view(torch.int32))
+    w = WORKLOADS["img2048_sparse"]
+    qw, kw, vw, mw = (t.to(DEV) for t in make_workload_inputs(w, seed=0))
+    a = dit.attn_fwd_blocksparse(qw, kw, vw, mw)
+    b = dit.attn_fwd_blocksparse(qw, kw, vw, mw)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
